@@ -1,0 +1,87 @@
+"""Run the fp64 oracle over many query rows in a process pool.
+
+TEST INFRASTRUCTURE ONLY (test suite, smoke check, benchmark CPU baseline).
+The arrays are written once to a temporary directory as .npy files and
+memory-mapped by each worker; workers are started with the "spawn" method so
+they never inherit a GPU context. Each worker evaluates a contiguous chunk of
+the requested rows with `qsa_oracle.sparse_prefill`, unchanged.
+"""
+import os
+import shutil
+import tempfile
+import time
+from concurrent.futures import ProcessPoolExecutor
+import multiprocessing as mp
+
+import numpy as np
+
+from . import qsa_oracle
+
+_ARRAYS = {}
+
+
+def default_workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _init(paths):
+    # one process per core: keep each worker's BLAS single-threaded
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:  # pragma: no cover
+        pass
+    for name, path in paths.items():
+        _ARRAYS[name] = np.load(path, mmap_mode="r")
+
+
+def _chunk(args):
+    rows, idx_rows, scale, q_pos0 = args
+    return qsa_oracle.sparse_prefill(_ARRAYS["q"], _ARRAYS["k"], _ARRAYS["v"], idx_rows, scale=scale,
+                                     rows=rows, q_pos0=q_pos0)
+
+
+def run_rows(q, k, v, idx_rows, rows, scale, q_pos0: int = 0, workers: int = None,
+             return_seconds: bool = False):
+    """Oracle outputs for query `rows`; idx_rows holds those rows' index lists.
+
+    Returns (out [R, Hq, 256] float64, lse [R, Hq] float64), plus the wall
+    time of the evaluation itself (excluding worker start-up) when asked.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    idx_rows = np.asarray(idx_rows)
+    assert idx_rows.shape[0] == rows.size
+    workers = default_workers() if workers is None else workers
+    if workers <= 1 or rows.size < 2:
+        t0 = time.perf_counter()
+        res = qsa_oracle.sparse_prefill(q, k, v, idx_rows, scale=scale, rows=rows, q_pos0=q_pos0)
+        dt = time.perf_counter() - t0
+        return (res + (dt,)) if return_seconds else res
+    tmp = tempfile.mkdtemp(prefix="qsa_oracle_", dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    try:
+        paths = {}
+        for name, a in (("q", q), ("k", k), ("v", v)):
+            paths[name] = os.path.join(tmp, name + ".npy")
+            np.save(paths[name], np.ascontiguousarray(a))
+        n_chunks = min(rows.size, workers * 4)
+        bounds = np.linspace(0, rows.size, n_chunks + 1).astype(int)
+        jobs = [(rows[a:b], idx_rows[a:b], scale, q_pos0) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+        with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn"),
+                                 initializer=_init, initargs=(paths,)) as ex:
+            list(ex.map(_init_probe, range(workers)))  # start every worker before timing
+            t0 = time.perf_counter()
+            parts = list(ex.map(_chunk, jobs))
+            dt = time.perf_counter() - t0
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    out = np.concatenate([p[0] for p in parts])
+    lse = np.concatenate([p[1] for p in parts])
+    return (out, lse, dt) if return_seconds else (out, lse)
+
+
+def _init_probe(_):
+    return len(_ARRAYS)

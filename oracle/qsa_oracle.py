@@ -77,14 +77,17 @@ def attend(q_h: np.ndarray, k_sel: np.ndarray, v_sel: np.ndarray, scale: float):
     return out, m + np.log(l), p
 
 
-def sparse_prefill(q, k, v, idx, scale: float = None, rows=None, Hq: int = None, Hkv: int = None):
+def sparse_prefill(q, k, v, idx, scale: float = None, rows=None, Hq: int = None, Hkv: int = None,
+                   q_pos0: int = 0):
     """Reference outputs of the QSA sparse-prefill operator.
 
-    q    [T, Hq, 256]   bf16 bits (uint16) or floats
-    k, v [T, Hkv, 256]  bf16 bits (uint16) or floats
-    idx  [T, Hkv, K]    int token positions (or [len(rows), Hkv, K] when
-                        `rows` is given and idx holds only those rows)
-    rows optional query rows to evaluate (default: all T rows)
+    q    [T, Hq, 256]     bf16 bits (uint16) or floats
+    k, v [T_kv, Hkv, 256] bf16 bits (uint16) or floats
+    idx  [T, Hkv, K]      int token positions (or [len(rows), Hkv, K] when
+                          `rows` is given and idx holds only those rows)
+    rows   optional query rows to evaluate (default: all T rows)
+    q_pos0 absolute position of query row 0 (tokens already in the cache);
+           query row t attends to positions 0 <= s <= q_pos0 + t
 
     Returns out float64 [R, Hq, 256] and lse float64 [R, Hq].
     """
@@ -103,16 +106,16 @@ def sparse_prefill(q, k, v, idx, scale: float = None, rows=None, Hq: int = None,
     else:
         rows = np.asarray(rows, dtype=np.int64)
         idx_rows = idx if idx.shape[0] == rows.size else idx[rows]
-    k64 = bf16_to_f64(k)
-    v64 = bf16_to_f64(v)
+    k = np.asarray(k)
+    v = np.asarray(v)
     out = np.zeros((rows.size, Hq, D))
     lse = np.full((rows.size, Hq), -np.inf)
     for i, t in enumerate(rows):
         q_t = bf16_to_f64(q[t])
         for g in range(Hkv):
-            sel = selected_positions(idx_rows[i, g], int(t))
-            k_sel = k64[sel, g, :] if sel else np.zeros((0, D))
-            v_sel = v64[sel, g, :] if sel else np.zeros((0, D))
+            sel = selected_positions(idx_rows[i, g], int(q_pos0) + int(t))
+            k_sel = bf16_to_f64(k[sel, g, :]) if sel else np.zeros((0, D))
+            v_sel = bf16_to_f64(v[sel, g, :]) if sel else np.zeros((0, D))
             for h in range(Hq):
                 if kv_head_of(h, G) != g:
                     continue

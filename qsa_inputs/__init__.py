@@ -22,7 +22,7 @@ Everything is NumPy on the host: arrays are returned as
   v   uint16 [T, Hkv, 256]  bf16 bit patterns
   idx int32  [T, Hkv, K]    token positions, -1 padded
 """
-from .configs import CONFIGS, Config, get_config
+from .configs import CONFIGS, EXTEND_CONFIG, Config, get_config
 from .generate import (
     make_inputs,
     make_qkv,
@@ -34,6 +34,7 @@ from .generate import (
 
 __all__ = [
     "CONFIGS",
+    "EXTEND_CONFIG",
     "Config",
     "get_config",
     "make_inputs",

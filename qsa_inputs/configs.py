@@ -41,11 +41,17 @@ class Config:
     outlier_scale: float = 1.0
     scale: float = 1.0 / 16.0
     oracle_rows: int = 0  # 0 = all rows; otherwise sampled rows for parity checks
+    q_pos0: int = 0  # absolute position of query row 0 (tokens already cached)
+    T_kv: int = 0  # K/V rows; 0 means T (no cached prefix)
     description: str = field(default="", compare=False)
 
     @property
     def G(self) -> int:
         return self.Hq // self.Hkv
+
+    @property
+    def kv_len(self) -> int:
+        return self.T_kv if self.T_kv else self.T
 
     @property
     def n_rest(self) -> int:
@@ -54,18 +60,21 @@ class Config:
     def shapes(self) -> dict:
         return {
             "q": (self.T, self.Hq, D),
-            "k": (self.T, self.Hkv, D),
-            "v": (self.T, self.Hkv, D),
+            "k": (self.kv_len, self.Hkv, D),
+            "v": (self.kv_len, self.Hkv, D),
             "idx": (self.T, self.Hkv, self.K),
             "out": (self.T, self.Hq, D),
             "lse": (self.T, self.Hq),
         }
 
     def valid_slots(self) -> int:
-        """Number of (t, kv head, slot) entries that are valid (0 <= s <= t)."""
-        T, K = self.T, self.K
-        ramp = min(T, K)
-        n = ramp * (ramp + 1) // 2 + max(0, T - K) * K
+        """Number of (t, kv head, slot) entries that are valid (0 <= s <= position)."""
+        n = 0
+        p0, p1, K = self.q_pos0, self.q_pos0 + self.T, self.K  # positions p0 .. p1-1
+        ramp_end = min(p1, K)  # positions p < K select p + 1 slots
+        if ramp_end > p0:
+            n += (ramp_end * (ramp_end + 1) - p0 * (p0 + 1)) // 2
+        n += max(0, p1 - max(p0, K)) * K
         return n * self.Hkv
 
     def gathered_bytes(self) -> int:
@@ -123,7 +132,20 @@ CONFIGS: Tuple[Config, ...] = (
     ),
 )
 
-_BY_NAME = {c.name: c for c in CONFIGS}
+# The long-prefill operator case the pages test: 7,810 query tokens against a
+# 65,536-token cache with 2,051 selected slots per query ("Nueve pruebas que
+# pasaron" section). Read as the last 7,810 tokens of a 65,536-token sequence.
+EXTEND_CONFIG = Config(
+    name="extend_t7810_kv65536_h12x1_k2051",
+    number=6,
+    T=7810, Hq=12, Hkv=1, K=2051,
+    window=512, sink=True, gap=0, sampler="uniform",
+    oracle_rows=512, q_pos0=65536 - 7810, T_kv=65536,
+    description="7,810 queries at positions 57,726..65,535 against a 65,536-token "
+                "K/V cache, (12,1), K=2051: 512-token window, sink 0, uniform rest",
+)
+
+_BY_NAME = {c.name: c for c in CONFIGS + (EXTEND_CONFIG,)}
 
 
 def get_config(key) -> Config:
@@ -131,10 +153,10 @@ def get_config(key) -> Config:
     if isinstance(key, Config):
         return key
     if isinstance(key, int):
-        return CONFIGS[key - 1]
+        return EXTEND_CONFIG if key == EXTEND_CONFIG.number else CONFIGS[key - 1]
     if isinstance(key, str):
         if key in _BY_NAME:
             return _BY_NAME[key]
         if key.startswith("c") and key[1:].isdigit():
-            return CONFIGS[int(key[1:]) - 1]
+            return get_config(int(key[1:]))
     raise KeyError(f"unknown workload {key!r}")

@@ -102,13 +102,12 @@ def make_qkv(cfg: Config, seed: int = None, workers=None):
     """
     cfg = get_config(cfg)
     seed = cfg.number if seed is None else seed
-    T, Hq, Hkv = cfg.T, cfg.Hq, cfg.Hkv
+    T, Hq, Hkv, Tk = cfg.T, cfg.Hq, cfg.Hkv, cfg.kv_len
     q = _normal_bf16(seed, STREAM_Q, T, Hq * D, workers).reshape(T, Hq, D)
-    k = _normal_bf16(seed, STREAM_K, T, Hkv * D, workers).reshape(T, Hkv, D)
-    v = _normal_bf16(seed, STREAM_V, T, Hkv * D, workers).reshape(T, Hkv, D)
-    if cfg.outlier_frac > 0.0 and T > 0:
-        n_out = int(round(cfg.outlier_frac * T))
-        pos = np.sort(_rng(seed, STREAM_OUTLIERS).choice(T, size=n_out, replace=False))
+    k = _normal_bf16(seed, STREAM_K, Tk, Hkv * D, workers).reshape(Tk, Hkv, D)
+    v = _normal_bf16(seed, STREAM_V, Tk, Hkv * D, workers).reshape(Tk, Hkv, D)
+    if cfg.outlier_frac > 0.0 and Tk > 0:
+        pos = outlier_positions(cfg, seed)
         for a in (k, v):
             a[pos] = f32_to_bf16_bits(bf16_bits_to_f32(a[pos]) * np.float32(cfg.outlier_scale))
     return q, k, v
@@ -117,10 +116,11 @@ def make_qkv(cfg: Config, seed: int = None, workers=None):
 def outlier_positions(cfg: Config, seed: int = None) -> np.ndarray:
     cfg = get_config(cfg)
     seed = cfg.number if seed is None else seed
-    if cfg.outlier_frac <= 0.0 or cfg.T == 0:
+    Tk = cfg.kv_len
+    if cfg.outlier_frac <= 0.0 or Tk == 0:
         return np.zeros(0, np.int64)
-    n_out = int(round(cfg.outlier_frac * cfg.T))
-    return np.sort(_rng(seed, STREAM_OUTLIERS).choice(cfg.T, size=n_out, replace=False))
+    n_out = int(round(cfg.outlier_frac * Tk))
+    return np.sort(_rng(seed, STREAM_OUTLIERS).choice(Tk, size=n_out, replace=False))
 
 
 # --------------------------------------------------------------------------- indices
@@ -179,9 +179,9 @@ def _weighted_distinct(rng, tt: np.ndarray, lo: int, hi: np.ndarray, m: int) -> 
 
 
 def _idx_chunk(job):
-    (seed, c, g, T, K, window, sink, gap, sampler) = job
+    (seed, c, g, T, K, window, sink, gap, sampler, q_pos0) = job
     t0, t1 = c * CHUNK, min(T, (c + 1) * CHUNK)
-    rows = np.arange(t0, t1, dtype=np.int64)
+    rows = np.arange(t0, t1, dtype=np.int64) + q_pos0  # absolute positions
     out = np.full((t1 - t0, K), -1, np.int32)
     if K == 0:
         return out
@@ -225,7 +225,7 @@ def make_indices(cfg: Config, seed: int = None, rows=None, workers=None) -> np.n
         raise ValueError("window + sink exceed the selection width")
     n_chunks = (T + CHUNK - 1) // CHUNK
     chunks = range(n_chunks) if rows is None else sorted(set(int(r) // CHUNK for r in rows))
-    jobs = [(seed, c, g, T, K, cfg.window, cfg.sink, cfg.gap, cfg.sampler)
+    jobs = [(seed, c, g, T, K, cfg.window, cfg.sink, cfg.gap, cfg.sampler, cfg.q_pos0)
             for c in chunks for g in range(Hkv)]
     parts = _map(_idx_chunk, jobs, workers)
     by_key = {(j[1], j[2]): p for j, p in zip(jobs, parts)}

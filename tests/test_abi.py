@@ -1,0 +1,110 @@
+"""The C ABI library: it loads, exports every entry point include/qsa.h
+declares, and rejects invalid arguments on the host before any HIP call
+(no GPU needed: every call here returns before touching a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_sparse_attention_qsa_amd as qsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+OK, INVALID, UNSUPPORTED, LAUNCH = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(qsa.library_path()):
+        pytest.fail("libqsa.so is not built: run __graft_entry__.build() first")
+    return qsa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(qsa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert names == ["qsa_abi_version", "qsa_sparse_prefill", "qsa_sparse_prefill_extend",
+                     "qsa_status_string"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libqsa.so does not export {name}"
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.qsa_abi_version() == 1
+    assert lib.qsa_status_string(OK) == b"ok"
+    assert lib.qsa_status_string(INVALID) == b"invalid argument"
+    assert lib.qsa_status_string(UNSUPPORTED) == b"unsupported size"
+    assert lib.qsa_status_string(LAUNCH) == b"kernel launch failed"
+    assert lib.qsa_status_string(99) == b"unknown status"
+
+
+# Distinct non-null host addresses stand in for device pointers: validation
+# rejects the call before any of them is used.
+P = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(7)]
+Q, K_, V, IDX, OUT, LSE, STREAM = P
+
+
+def call(lib, q=Q, k=K_, v=V, idx=IDX, T=8, Hq=4, Hkv=2, K=5, scale=0.0625, out=OUT, lse=LSE):
+    return lib.qsa_sparse_prefill(q, k, v, idx, T, Hq, Hkv, K, scale, out, lse, None)
+
+
+def call_ext(lib, T=8, T_kv=20, p0=4, Hq=4, Hkv=2, K=5, scale=0.0625, q=Q, out=OUT):
+    return lib.qsa_sparse_prefill_extend(q, K_, V, IDX, T, T_kv, p0, Hq, Hkv, K, scale, out, LSE, None)
+
+
+@pytest.mark.parametrize("kwargs", [
+    dict(T=-1), dict(T=2 ** 31), dict(Hq=0), dict(Hkv=0), dict(Hq=-3), dict(K=-1),
+    dict(Hq=6, Hkv=4), dict(Hq=3, Hkv=2), dict(scale=float("nan")), dict(scale=float("inf")),
+    dict(scale=float("-inf")), dict(q=None), dict(out=None), dict(lse=None), dict(k=None),
+    dict(v=None), dict(idx=None), dict(out=Q), dict(out=K_), dict(lse=IDX), dict(lse=OUT),
+])
+def test_invalid_arguments_are_rejected(lib, kwargs):
+    assert call(lib, **kwargs) == INVALID
+
+
+def test_unsupported_sizes(lib):
+    # T * Hkv * 512 bytes of K must stay below 2^31
+    assert call(lib, T=4194304, Hq=1, Hkv=1) == UNSUPPORTED
+    assert call(lib, T=2097152, Hq=4, Hkv=2) == UNSUPPORTED
+    assert call(lib, K=(1 << 28) + 1) == UNSUPPORTED
+
+
+def test_zero_tokens_is_a_noop(lib):
+    assert call(lib, T=0) == OK
+    assert call(lib, T=0, q=None, k=None, v=None, idx=None, out=None, lse=None) == OK
+
+
+def test_null_index_rejected_only_when_used(lib):
+    # K == 0: idx, k and v are never read; with T == 0 nothing is launched either
+    assert call(lib, T=0, K=0, idx=None) == OK
+
+
+@pytest.mark.parametrize("kwargs,expect", [
+    (dict(p0=-1), INVALID), (dict(T=8, T_kv=11, p0=4), INVALID), (dict(T_kv=-2), INVALID),
+    (dict(T=0, T_kv=0, p0=0), OK), (dict(T=0, T_kv=100, p0=100), OK),
+    (dict(T=8, T_kv=4194304, p0=0, Hkv=1, Hq=1), UNSUPPORTED),
+])
+def test_extend_argument_rules(lib, kwargs, expect):
+    assert call_ext(lib, **kwargs) == expect
+
+
+def test_python_binding_validates_before_calling():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(4, 2, 256, dtype=torch.bfloat16)
+    k = torch.zeros(4, 1, 256, dtype=torch.bfloat16)
+    idx = torch.zeros(4, 1, 3, dtype=torch.int32)
+    with pytest.raises(ValueError):  # host tensors are refused
+        qsa.sparse_prefill(q, k, k, idx)
+    with pytest.raises(TypeError):
+        qsa.sparse_prefill(q.float(), k, k, idx)
+    with pytest.raises(TypeError):
+        qsa.sparse_prefill(q, k, k, idx.long())

@@ -113,6 +113,43 @@ def test_explicit_scale_matches_torch_sdpa(scale):
     np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("T_kv,T,p0", [(40, 12, 28), (33, 33, 0), (50, 7, 20)])
+def test_extend_over_cached_prefix_matches_masked_sdpa(T_kv, T, p0):
+    """Queries at positions p0..p0+T-1 against a longer cache, every position
+    <= the query's selected: torch fp64 attention with an explicit mask."""
+    rng = np.random.default_rng(T_kv * 7 + p0)
+    q = _rand_bf16(rng, (T, 4, D))
+    k = _rand_bf16(rng, (T_kv, 2, D))
+    v = _rand_bf16(rng, (T_kv, 2, D))
+    K = T_kv + 3
+    idx = np.full((T, 2, K), -1, np.int32)
+    for t in range(T):
+        for g in range(2):
+            row = np.full(K, -1, np.int32)
+            row[: p0 + t + 1] = np.arange(p0 + t + 1)
+            rng.shuffle(row)
+            idx[t, g] = row
+    out, lse = oracle.sparse_prefill(q, k, v, idx, scale=1 / 16, q_pos0=p0)
+    Q = torch.from_numpy(qo.bf16_to_f64(q)).permute(1, 0, 2)
+    Kr = torch.from_numpy(qo.bf16_to_f64(k)).repeat_interleave(2, dim=1).permute(1, 0, 2)
+    Vr = torch.from_numpy(qo.bf16_to_f64(v)).repeat_interleave(2, dim=1).permute(1, 0, 2)
+    allowed = torch.arange(T_kv)[None, :] <= (p0 + torch.arange(T))[:, None]
+    ref = F.scaled_dot_product_attention(Q, Kr, Vr, attn_mask=allowed, scale=1 / 16)
+    scores = torch.matmul(Q, Kr.transpose(1, 2).contiguous()) / 16
+    ref_lse = torch.logsumexp(scores.masked_fill(~allowed, float("-inf")), dim=-1)
+    np.testing.assert_allclose(out, ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse.permute(1, 0).numpy(), rtol=0, atol=1e-12)
+
+
+def test_extend_equals_rows_of_full_prefill():
+    rng, q, k, v, idx = _sparse_case(seed=31, T=80, Hq=6, Hkv=2, K=30)
+    full_out, full_lse = oracle.sparse_prefill(q, k, v, idx, scale=1 / 16)
+    p0 = 53
+    out, lse = oracle.sparse_prefill(q[p0:], k, v, idx[p0:], scale=1 / 16, q_pos0=p0)
+    np.testing.assert_array_equal(out, full_out[p0:])
+    np.testing.assert_array_equal(lse, full_lse[p0:])
+
+
 # ----------------------------------------------------------------- sparse invariants
 
 

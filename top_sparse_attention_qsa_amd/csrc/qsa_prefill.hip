@@ -1,0 +1,351 @@
+// QSA sparse-attention prefill for MI355X (gfx950, CDNA4, wave64).
+//
+// Operation: "Qwen4-Exp QSA llega al Ascend de Huawei" (orcarouter.ai, Spanish
+// page), section "Lo que realmente añade la pull request" -- per query token t
+// and query head h, softmax(scale * q . K_sel^T) . V_sel over the positions an
+// indexer selected for (t, KV head of h); -1 slots masked, an empty row gives
+// zero. Positions above t are masked too (causal prefill).
+//
+// Work decomposition. One wavefront owns one work item (t, g, head chunk):
+// the G = Hq/Hkv query heads of KV head g (at most 16 per chunk) against the K
+// selected slots of (t, g). Items are independent, so waves never synchronise
+// with each other; a block is WPB such waves.
+//
+// Per wave, the K list is walked in tiles of 16 slots:
+//   1. one buffer load brings the tile's indices, lane l holding slot l & 15;
+//      slots past K read as 0 (range check) and are masked by position;
+//      validity 0 <= s <= t gives a 16-bit mask (ballot);
+//   2. lane (jg, hl) = (l >> 4, l & 15) loads 16-byte chunks 4c + jg,
+//      c = 0..7, of key row hl from K and from V (512 B per row). For K this
+//      is directly the A-operand layout of the score MFMA; V goes through LDS.
+//      A masked slot gets a byte offset past the end of the buffer: the range
+//      check returns zeros and nothing is fetched;
+//   3. S^T = K_tile . Q_g^T on v_mfma_f32_16x16x32_bf16: keys are the M side,
+//      the head group (zero-padded to 16) is N, d = 256 is the contraction.
+//      Q lives in registers for the whole item;
+//   4. online softmax in fp32, base 2. In the S^T layout a lane holds 4 keys
+//      of one head: the row max is an in-lane max plus two cross-lane steps;
+//      the row sum stays per lane until the epilogue. The reference max only
+//      moves when a tile max exceeds it by a slack of 2^8, so rescaling the
+//      accumulators is rare;
+//   5. O^T += V_tile^T . P^T on v_mfma_f32_16x16x16_bf16: V^T comes out of
+//      LDS with ds_read_b64_tr_b16 (a 4x16 bf16 block transposed across 16
+//      lanes); P^T is already in the B-operand layout, so a head's max, sum and
+//      output stay in that head's lanes;
+//   6. epilogue: O / l rounded to bf16 (RNE), lse = ln 2 * (m + log2 l); an
+//      empty row writes +0.0 and -inf.
+// The loads of tile j+1 are issued as soon as the score MFMAs of tile j have
+// read its K registers, and are in flight during the rest of tile j.
+
+#include "qsa_internal.h"
+
+#include <math.h>
+
+namespace qsa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
+constexpr int kD = 256;
+constexpr int kRowBytes = 512;              // one head's K or V row
+constexpr int kNK = 16;                     // selected slots per tile
+constexpr uint32_t kOob = 0x80000000u;      // byte offset beyond every K/V buffer
+constexpr uint32_t kRsrcFlags = 0x00020000u; // raw buffer, 32-bit data format (gfx9)
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kRescaleSlack = 8.f;         // log2 headroom before the running max moves
+
+struct KParams {
+    const uint16_t *q;
+    const uint8_t *k;
+    const uint8_t *v;
+    const int32_t *idx;
+    uint16_t *out;
+    float *lse;
+    int64_t q_pos0;
+    int32_t n_items; // T * Hkv * n_hchunks
+    int32_t Hq, Hkv, K, G, n_hchunks;
+    uint32_t kv_bytes;  // T_kv * Hkv * 512
+    float scale_log2;   // scale * log2(e)
+};
+
+// Blocks are dealt round-robin over the 8 XCDs (block b runs on XCD b % 8).
+// Renumber so each XCD works on one contiguous range of items: neighbouring
+// query positions share their local window and sink rows in that XCD's L2.
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t nb) {
+    const uint32_t q = nb >> 3, r = nb & 7u;
+    const uint32_t x = b & 7u, i = b >> 3;
+    return x * q + (x < r ? x : r) + i;
+}
+
+__device__ __forceinline__ float wave_max_across_groups(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_across_groups(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Indices of one tile: lane l reads slot j*16 + (l & 15), so every lane holds
+// the position of the key row it will load. Slots past K read as 0 (buffer
+// range check) and are masked by position.
+__device__ __forceinline__ int32_t load_tile_idx(__amdgpu_buffer_rsrc_t ri, int j, int lane) {
+    return __builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)(j * kNK + (lane & 15)) * 4u, 0, 0);
+}
+
+// K and V of one tile. Lane (jg, hl) loads chunks 4c + jg (c = 0..7) of key
+// row hl: that is the A-operand layout of the score MFMA for K, and for V the
+// same 16 B go to LDS. `off` is the row's byte offset, or kOob for a masked
+// slot (the buffer range check then returns zeros and fetches nothing).
+__device__ __forceinline__ void load_tile_kv(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                             uint32_t off, u32x4_t (&ka)[8], u32x4_t (&vs)[8],
+                                             int lane) {
+    const uint32_t o = off + (uint32_t)((lane >> 4) << 4);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ka[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, o + c * 64, 0, 0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) vs[c] = __builtin_amdgcn_raw_buffer_load_b128(rv, o + c * 64, 0, 0);
+}
+
+struct SoftmaxState {
+    float m;   // reference max of the base-2 logits (same in every lane of a head)
+    float l;   // this lane's share of the sum of the weights as fed to the MFMA
+    float le;  // this lane's share of the sum of the fp32 weights (for lse)
+};
+
+// Swizzle of the V tile in LDS: row r keeps 16-byte chunk c at c ^ vswz(r).
+// vswz is a bijection on 0..15 (the 16 rows of a store phase hit distinct
+// banks) and vswz(r) >> 1 = r & 7 (the 8 rows of a transposed-read phase read
+// distinct 32-byte slots).
+__device__ __forceinline__ int vswz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+__device__ __forceinline__ void store_tile_v(uint8_t *lv, const u32x4_t (&vs)[8], int lane) {
+    const int hl = lane & 15;
+    const int jg = lane >> 4;
+    uint8_t *row = lv + hl * kRowBytes;
+    const int sw = vswz(hl);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) *(u32x4_t *)(row + (((4 * c + jg) ^ sw) << 4)) = vs[c];
+}
+
+// Scores of one 16-key tile: S^T[key][head], lane (jg, hl) getting keys
+// jg*4 + r (r = 0..3) of head hl.
+__device__ __forceinline__ f32x4_t tile_scores(const u32x4_t (&ka)[8], const bf16x8_t (&qb)[8]) {
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[c]), qb[c], s, 0, 0, 0);
+    return s;
+}
+
+// Online softmax and weighted values of one 16-key tile whose V is in LDS.
+template <bool kSplitP>
+__device__ __forceinline__ void tile_finish(f32x4_t s, const uint8_t *lv, uint32_t mask,
+                                            f32x4_t (&o)[16], SoftmaxState &st, float scale_log2,
+                                            int lane) {
+    const int hl = lane & 15;
+    const int jg = lane >> 4;
+
+    float x[4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        x[r] = ((mask >> (jg * 4 + r)) & 1u) ? s[r] * scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, x[r]);
+    }
+    // The tile has at least one valid key (the caller skips empty tiles), so
+    // tmax is finite for every head. The reference max only moves when a
+    // head's tile max exceeds it by more than kRescaleSlack (base-2 units):
+    // weights stay below 2^kRescaleSlack and the O/l rescale is rare.
+    tmax = wave_max_across_groups(tmax);
+    if (__ballot(tmax > st.m + kRescaleSlack)) {
+        const float m_new = fmaxf(st.m, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(st.m - m_new); // 0 on the first tile
+        st.l *= alpha;
+        st.le *= alpha;
+        st.m = m_new;
+#pragma unroll
+        for (int db = 0; db < 16; ++db) o[db] *= alpha;
+    }
+
+    // Weights go to the MFMA as bf16. The output is normalised by the sum of
+    // exactly those values (a convex combination of V rows whatever the
+    // rounding); lse uses the fp32 sum. With kSplitP the weight is sent as
+    // hi + lo, two bf16 terms, and both sums agree to ~2^-17.
+    bf16x4_t pb;
+    bf16x4_t pl;
+    float psum = 0.f, esum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float pe = __builtin_amdgcn_exp2f(x[r] - st.m);
+        const __bf16 hi = (__bf16)pe;
+        pb[r] = hi;
+        esum += pe;
+        if constexpr (kSplitP) {
+            const __bf16 lo = (__bf16)(pe - (float)hi);
+            pl[r] = lo;
+            psum += (float)hi + (float)lo;
+        } else {
+            psum += (float)hi;
+        }
+    }
+    st.l += psum;
+    st.le += esum;
+
+    // V^T operand of O^T += V^T P^T (16x16x16): lane (jg, hl) addresses row
+    // jg*4 + (hl >> 2), 8 bytes at d = db*16 + (hl & 3)*4; the transposed read
+    // returns column d = db*16 + hl of rows jg*4 + 0..3.
+    const int R = jg * 4 + (hl >> 2);
+    const int sw = vswz(R);
+    const uint8_t *vrow = lv + R * kRowBytes + (hl & 1) * 8;
+    const int half = (hl & 3) >> 1;
+    const i16x4_t pbi = __builtin_bit_cast(i16x4_t, pb);
+    const i16x4_t pli = __builtin_bit_cast(i16x4_t, pl);
+#pragma unroll
+    for (int db = 0; db < 16; ++db) {
+        const int ch = (2 * db + half) ^ sw;
+        const bf16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(vrow + (ch << 4)));
+        const i16x4_t vai = __builtin_bit_cast(i16x4_t, va);
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vai, pbi, o[db], 0, 0, 0);
+        if constexpr (kSplitP) o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vai, pli, o[db], 0, 0, 0);
+    }
+}
+
+template <int WPB, bool kSplitP>
+__global__ __launch_bounds__(64 * WPB) void qsa_prefill_kernel(const KParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_v[WPB][kNK * kRowBytes];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int32_t item = (int32_t)xcd_contiguous(blockIdx.x, gridDim.x) * WPB + w;
+    if (item >= p.n_items) return;
+
+    const int32_t hc = item % p.n_hchunks;
+    const int32_t rest = item / p.n_hchunks;
+    const int32_t g = rest % p.Hkv;
+    const int32_t row = rest / p.Hkv;
+    const int64_t tq = p.q_pos0 + row; // absolute position of this query
+    const int h0 = g * p.G + hc * 16;
+    const int nh = min(16, p.G - hc * 16);
+    const int hl = lane & 15;
+    const int jg = lane >> 4;
+
+    // Q group as the B operand: lane (jg, hl) holds head hl, d = c*32 + jg*8 .. +8.
+    bf16x8_t qb[8];
+    if (hl < nh) {
+        const uint16_t *qrow = p.q + ((int64_t)row * p.Hq + h0 + hl) * kD + jg * 8;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) qb[c] = *(const bf16x8_t *)(qrow + c * 32);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            for (int e = 0; e < 8; ++e) qb[c][e] = (__bf16)0.f;
+    }
+
+    f32x4_t o[16];
+#pragma unroll
+    for (int db = 0; db < 16; ++db) o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    SoftmaxState st = {-INFINITY, 0.f, 0.f};
+
+    const int K = p.K;
+    const int n_tiles = (K + kNK - 1) / kNK;
+    if (n_tiles > 0) {
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)p.k, 0, (int)p.kv_bytes, kRsrcFlags);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)p.v, 0, (int)p.kv_bytes, kRsrcFlags);
+        const int32_t *irow = p.idx + ((int64_t)row * p.Hkv + g) * K;
+        const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc((void *)irow, 0, K * 4, kRsrcFlags);
+        const uint32_t row_stride = (uint32_t)p.Hkv * kRowBytes;
+        const uint32_t head_off = (uint32_t)g * kRowBytes;
+        uint8_t *lv = &lds_v[w][0];
+
+        // Row byte offset of this lane's slot in tile j (kOob when masked) and
+        // the tile's validity mask (bit k = key k of the tile).
+        auto prep = [&](int j, int32_t s, uint32_t &mask) -> uint32_t {
+            const bool ok = (j * kNK + hl < K) && (s >= 0) && ((int64_t)s <= tq);
+            mask = (uint32_t)__ballot(ok) & 0xFFFFu;
+            return ok ? (uint32_t)s * row_stride + head_off : kOob;
+        };
+
+        // The loads of tile j+1 are issued right after the score MFMAs of tile
+        // j have consumed its K registers, and are in flight during the
+        // softmax and weighted-value MFMAs of tile j.
+        u32x4_t ka[8], vs[8];
+        uint32_t mask = 0, mask_next = 0;
+        int32_t inext = load_tile_idx(ri, 0, lane);
+        uint32_t off = prep(0, inext, mask);
+        load_tile_kv(rk, rv, off, ka, vs, lane);
+        inext = load_tile_idx(ri, 1, lane);
+        for (int j = 0;; ++j) {
+            store_tile_v(lv, vs, lane);
+            f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+            if (mask) sc = tile_scores(ka, qb);
+            // Issued even past the last tile (all slots masked there: nothing
+            // is fetched), so the register flow is the same in every iteration.
+            off = prep(j + 1, inext, mask_next);
+            load_tile_kv(rk, rv, off, ka, vs, lane);
+            inext = load_tile_idx(ri, j + 2, lane);
+            if (mask) tile_finish<kSplitP>(sc, lv, mask, o, st, p.scale_log2, lane);
+            if (j + 1 >= n_tiles) break;
+            mask = mask_next;
+        }
+    }
+
+    const float l_tot = wave_sum_across_groups(st.l);
+    const float le_tot = wave_sum_across_groups(st.le);
+    if (hl < nh) {
+        const int64_t orow = (int64_t)row * p.Hq + h0 + hl;
+        uint16_t *optr = p.out + orow * kD + jg * 4;
+        const bool empty = !(l_tot > 0.f);
+        const float inv = empty ? 0.f : 1.0f / l_tot;
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+            bf16x4_t r4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) r4[r] = (__bf16)(o[db][r] * inv);
+            *(bf16x4_t *)(optr + db * 16) = r4;
+        }
+        if (jg == 0) p.lse[orow] = empty ? -INFINITY : (st.m + __log2f(le_tot)) * kLn2;
+    }
+}
+
+template <int WPB, bool kSplitP>
+qsa_status_t launch(const KParams &kp, hipStream_t stream) {
+    const uint32_t blocks = (uint32_t)((kp.n_items + WPB - 1) / WPB);
+    hipLaunchKernelGGL((qsa_prefill_kernel<WPB, kSplitP>), dim3(blocks), dim3(64 * WPB), 0, stream, kp);
+    return hipGetLastError() == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH;
+}
+
+} // namespace
+
+qsa_status_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
+    KParams kp;
+    kp.q = (const uint16_t *)a.q;
+    kp.k = (const uint8_t *)a.k;
+    kp.v = (const uint8_t *)a.v;
+    kp.idx = a.idx;
+    kp.out = (uint16_t *)a.out;
+    kp.lse = a.lse;
+    kp.q_pos0 = a.q_pos0;
+    kp.Hq = a.Hq;
+    kp.Hkv = a.Hkv;
+    kp.K = a.K;
+    kp.G = a.Hq / a.Hkv;
+    kp.n_hchunks = (kp.G + 15) / 16;
+    const int64_t n_items = a.T * a.Hkv * kp.n_hchunks;
+    if (n_items > INT32_MAX) return QSA_ERR_UNSUPPORTED;
+    kp.n_items = (int32_t)n_items;
+    kp.kv_bytes = (uint32_t)(a.T_kv * a.Hkv * kRowBytes);
+    kp.scale_log2 = a.scale * 1.44269504088896340736f;
+    return launch<4, true>(kp, stream);
+}
+
+} // namespace qsa
