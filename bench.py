@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the QSA sparse-prefill operator on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload c4]
+
+A step is one call of the operator over the whole workload (all query tokens,
+all heads): gather the selected K/V rows, scores, softmax, weighted values,
+outputs. Inputs are generated on the host (seeded, synthetic), copied to HBM
+once, and resident before the timed region starts. Prints one JSON line.
+
+Default workload: T = 32768 query tokens, (Hq, Hkv) = (24, 2) -- the
+24-query / 2-KV-head model of "Qwen4-Exp QSA llega al Ascend de Huawei",
+section "Por qué QSA es la parte incómoda, en cifras" -- K = 2048 selected
+slots per (token, KV head) (the page's 2,048 budget), head dim 256, bf16.
+
+Roofline: the kernel is bound by HBM bandwidth on the gathered rows. Per
+valid slot it must gather 512 B of K and 512 B of V; `achieved` is those
+algorithmic bytes per launch divided by the mean kernel duration, measured
+with HIP events on the stream the kernel runs on, against MI355X's 8 TB/s.
+`traffic` comes from committed rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs
+of this same command, scaled by the counters' reading on a copy kernel of
+known size, and is reported only while the kernel source still matches the
+one the counters were taken on.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ("top_sparse_attention_qsa_amd/csrc/qsa_prefill.hip",)
+METRIC = "QSA sparse prefill query-tokens/s and gathered-KV GB/s (% HBM roofline), 1 GPU"
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def measured_traffic(workload: str, sha: str):
+    """Bytes per launch moved past L2 (FETCH_SIZE + WRITE_SIZE, calibrated), from the
+    committed counter summary of this workload, or None when absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"qsa_prefill_kernel_{workload}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_sha") != sha:
+        return None
+    return int(round(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]))
+
+
+def cpu_baseline(cfg, q, k, v, idx, n_rows: int):
+    """The fp64 oracle, as it is, on a seeded sample of the workload's rows."""
+    import numpy as np
+    from oracle import pool
+    from qsa_inputs import sample_rows
+
+    rows = sample_rows(cfg, n=n_rows, seed=cfg.number + 1000)
+    rows = rows[:n_rows]
+    workers = pool.default_workers()
+    _, _, secs = pool.run_rows(q, k, v, idx[rows], rows, cfg.scale, q_pos0=cfg.q_pos0,
+                               workers=workers, return_seconds=True)
+    return {
+        "value": round(float(rows.size / secs), 3),
+        "unit": "query-tokens/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"{rows.size} seeded rows of {cfg.name} (all {cfg.Hq} heads each), fp64 NumPy, "
+                  f"one process per core, BLAS single-threaded; {secs:.2f} s wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c4", help="c1..c5 or a workload name (default c4)")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="rows for the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the operator "
+              "would shard over query rows or KV heads with no exchange after the kernel). "
+              "Run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be >= 1 and --warmup >= 0")
+
+    import numpy as np
+    import torch
+
+    import top_sparse_attention_qsa_amd as qsa
+    from qsa_inputs import get_config, make_indices, make_qkv
+
+    cfg = get_config(args.workload)
+    t0 = time.perf_counter()
+    q, k, v = make_qkv(cfg)
+    idx = make_indices(cfg)
+    log(f"{cfg.name}: inputs generated in {time.perf_counter() - t0:.1f}s")
+
+    cpu = None
+    if not args.no_cpu_baseline and args.cpu_rows > 0:
+        t0 = time.perf_counter()
+        cpu = cpu_baseline(cfg, q, k, v, idx, args.cpu_rows)
+        log(f"cpu baseline {cpu['value']} q-tok/s on {cpu['cores']} cores ({time.perf_counter() - t0:.1f}s)")
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (no HIP device visible)", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    qsa.load_library()
+    to_bf16 = lambda a: torch.from_numpy(a).view(torch.bfloat16).to(dev)
+    dq, dk, dv = to_bf16(q), to_bf16(k), to_bf16(v)
+    didx = torch.from_numpy(idx).to(dev)
+    out = torch.empty((cfg.T, cfg.Hq, 256), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((cfg.T, cfg.Hq), dtype=torch.float32, device=dev)
+    del q, k, v, idx
+
+    def step():
+        if cfg.q_pos0:
+            qsa.sparse_prefill_extend(dq, dk, dv, didx, cfg.q_pos0, scale=cfg.scale, out=out, lse=lse)
+        else:
+            qsa.sparse_prefill(dq, dk, dv, didx, scale=cfg.scale, out=out, lse=lse)
+
+    # a plain copy of known size: context for the bandwidth and the counters' scale
+    copy_bytes = 1 << 30
+    src = torch.empty(copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * copy_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    cold0, cold1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cold0.record(stream)
+    step()
+    cold1.record(stream)
+    for _ in range(max(0, args.warmup - 1)):
+        step()
+    torch.cuda.synchronize()
+    first_ms = cold0.elapsed_time(cold1)
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+
+    ms_per_step = wall * 1e3 / args.steps
+    gathered = cfg.gathered_bytes()
+    kernel_s = float(kms.mean()) * 1e-3
+    achieved = gathered / kernel_s / 1e9
+    sha = kernel_sha()
+    traffic = measured_traffic(cfg.name, sha)
+    qtok_s = cfg.T / (ms_per_step * 1e-3)
+
+    res = {
+        "metric": METRIC,
+        "value": round(qtok_s, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "T": cfg.T, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "head_dim": 256, "K": cfg.K,
+            "q_pos0": cfg.q_pos0, "T_kv": cfg.kv_len, "scale": cfg.scale,
+            "index_lists": cfg.description,
+            "valid_slots": cfg.valid_slots(),
+            "parallelism": "single GPU",
+        },
+        "gathered_kv_GBps": round(gathered / (ms_per_step * 1e-3) / 1e9, 1),
+        "hbm_roofline_frac": round(gathered / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "qsa_prefill_kernel",
+            "algorithmic_bytes_per_launch": gathered,
+            "kernel_ms_mean": round(float(kms.mean()), 4),
+            "kernel_ms_min": round(float(kms.min()), 4),
+            "kernel_ms_median": round(float(np.median(kms)), 4),
+            "kernel_sha": sha,
+        },
+        "first_call_ms": round(first_ms, 3),
+        "copy_GBps": round(copy_gbps, 1),
+        "useful_tflops": round(cfg.useful_flops() / kernel_s / 1e12, 2),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
