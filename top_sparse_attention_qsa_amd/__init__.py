@@ -43,12 +43,15 @@ def library_path() -> str:
     return os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libqsa.so")
 
 
-def load_library():
-    """Load libqsa.so (built by top_sparse_attention_qsa_amd.build) once."""
+def load_library(path: str = None):
+    """Load libqsa.so (built by top_sparse_attention_qsa_amd.build) once.
+
+    `path` selects another build of the same ABI (used to compare kernel
+    builds side by side); it replaces the library used by this module."""
     global _LIB
-    if _LIB is not None:
+    if _LIB is not None and path is None:
         return _LIB
-    path = library_path()
+    path = library_path() if path is None else path
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m top_sparse_attention_qsa_amd.build` "

@@ -9,33 +9,45 @@
 // Work decomposition. One wavefront owns one work item (t, g, head chunk):
 // the G = Hq/Hkv query heads of KV head g (at most 16 per chunk) against the K
 // selected slots of (t, g). Items are independent, so waves never synchronise
-// with each other; a block is WPB such waves.
+// with each other; a block is WPB such waves. Blocks are renumbered so that
+// each XCD (block b runs on XCD b % 8) works through one contiguous range of
+// items: neighbouring query positions share their local window and sink rows
+// in that XCD's L2.
 //
 // Per wave, the K list is walked in tiles of 16 slots:
 //   1. one buffer load brings the tile's indices, lane l holding slot l & 15;
 //      slots past K read as 0 (range check) and are masked by position;
 //      validity 0 <= s <= t gives a 16-bit mask (ballot);
-//   2. lane (jg, hl) = (l >> 4, l & 15) loads 16-byte chunks 4c + jg,
-//      c = 0..7, of key row hl from K and from V (512 B per row). For K this
-//      is directly the A-operand layout of the score MFMA; V goes through LDS.
-//      A masked slot gets a byte offset past the end of the buffer: the range
-//      check returns zeros and nothing is fetched;
+//   2. the 16 K rows and 16 V rows (512 B each) are gathered row-contiguously:
+//      each 16-byte load instruction covers two whole rows, lane l reading
+//      chunk l & 31 of row 2i + (l >> 5), so every quad of lanes reads 64
+//      contiguous bytes and the vector L1 sees whole-line accesses. A masked
+//      slot gets a byte offset past the end of the buffer: the range check
+//      returns zeros and nothing is fetched. The tile goes to registers, then
+//      to two swizzled LDS tiles (K and V), from which the MFMA operands are
+//      read in their own layouts;
 //   3. S^T = K_tile . Q_g^T on v_mfma_f32_16x16x32_bf16: keys are the M side,
 //      the head group (zero-padded to 16) is N, d = 256 is the contraction.
 //      Q lives in registers for the whole item;
 //   4. online softmax in fp32, base 2. In the S^T layout a lane holds 4 keys
 //      of one head: the row max is an in-lane max plus two cross-lane steps;
-//      the row sum stays per lane until the epilogue. The reference max only
+//      the row sums stay per lane until the epilogue. The reference max only
 //      moves when a tile max exceeds it by a slack of 2^8, so rescaling the
 //      accumulators is rare;
 //   5. O^T += V_tile^T . P^T on v_mfma_f32_16x16x16_bf16: V^T comes out of
 //      LDS with ds_read_b64_tr_b16 (a 4x16 bf16 block transposed across 16
-//      lanes); P^T is already in the B-operand layout, so a head's max, sum and
-//      output stay in that head's lanes;
+//      lanes); P^T is already in the B-operand layout. Each weight is sent as
+//      a hi + lo pair of bf16 values (two MFMAs), so the weights carry ~16
+//      significant bits into the fp32 accumulator;
 //   6. epilogue: O / l rounded to bf16 (RNE), lse = ln 2 * (m + log2 l); an
 //      empty row writes +0.0 and -inf.
-// The loads of tile j+1 are issued as soon as the score MFMAs of tile j have
-// read its K registers, and are in flight during the rest of tile j.
+// The loads of tile j+1 are issued right after tile j has been written to
+// LDS and are in flight while tile j is computed; indices run two tiles ahead.
+//
+// LDS bank layout. Row r of the K tile keeps 16-byte chunk c at c ^ (r & 15),
+// row r of the V tile at c ^ vswz(r). The row-contiguous stores, the K
+// operand reads (16 rows, one chunk) and the transposed V reads (4 or 8 rows,
+// 32 bytes each) then hit distinct banks in every phase.
 
 #include "qsa_internal.h"
 
@@ -102,18 +114,39 @@ __device__ __forceinline__ int32_t load_tile_idx(__amdgpu_buffer_rsrc_t ri, int 
     return __builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)(j * kNK + (lane & 15)) * 4u, 0, 0);
 }
 
-// K and V of one tile. Lane (jg, hl) loads chunks 4c + jg (c = 0..7) of key
-// row hl: that is the A-operand layout of the score MFMA for K, and for V the
-// same 16 B go to LDS. `off` is the row's byte offset, or kOob for a masked
-// slot (the buffer range check then returns zeros and fetches nothing).
+// K and V of one tile, row-contiguous. Instruction i covers rows 2i and
+// 2i+1: lane l reads 16-byte chunk l & 31 of row 2i + (l >> 5). `off` holds,
+// in lane r < 16, the byte offset of key row r (kOob when masked).
 __device__ __forceinline__ void load_tile_kv(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                             uint32_t off, u32x4_t (&ka)[8], u32x4_t (&vs)[8],
+                                             uint32_t off, u32x4_t (&ks)[8], u32x4_t (&vs)[8],
                                              int lane) {
-    const uint32_t o = off + (uint32_t)((lane >> 4) << 4);
+    const bool upper = (lane >> 5) != 0;
+    const uint32_t ch = (uint32_t)(lane & 31) << 4;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) ka[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, o + c * 64, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t o0 = __builtin_amdgcn_readlane(off, 2 * i);
+        const uint32_t o1 = __builtin_amdgcn_readlane(off, 2 * i + 1);
+        const uint32_t o = (upper ? o1 : o0) + ch;
+        ks[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
+        vs[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0);
+    }
+}
+
+// V tile swizzle: row r keeps 16-byte chunk c at c ^ vswz(r). vswz(r) >> 1 =
+// r & 7, so the 4 (or 8) rows of a transposed-read phase read distinct
+// 32-byte slots.
+__device__ __forceinline__ int vswz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+__device__ __forceinline__ void store_tile_kv(uint8_t *lk, uint8_t *lv, const u32x4_t (&ks)[8],
+                                              const u32x4_t (&vs)[8], int lane) {
+    const int half = lane >> 5;
+    const int c = lane & 31;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) vs[c] = __builtin_amdgcn_raw_buffer_load_b128(rv, o + c * 64, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+        const int r = 2 * i + half;
+        *(u32x4_t *)(lk + r * kRowBytes + ((c ^ (r & 15)) << 4)) = ks[i];
+        *(u32x4_t *)(lv + r * kRowBytes + ((c ^ vswz(r)) << 4)) = vs[i];
+    }
 }
 
 struct SoftmaxState {
@@ -122,28 +155,19 @@ struct SoftmaxState {
     float le;  // this lane's share of the sum of the fp32 weights (for lse)
 };
 
-// Swizzle of the V tile in LDS: row r keeps 16-byte chunk c at c ^ vswz(r).
-// vswz is a bijection on 0..15 (the 16 rows of a store phase hit distinct
-// banks) and vswz(r) >> 1 = r & 7 (the 8 rows of a transposed-read phase read
-// distinct 32-byte slots).
-__device__ __forceinline__ int vswz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-
-__device__ __forceinline__ void store_tile_v(uint8_t *lv, const u32x4_t (&vs)[8], int lane) {
-    const int hl = lane & 15;
-    const int jg = lane >> 4;
-    uint8_t *row = lv + hl * kRowBytes;
-    const int sw = vswz(hl);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) *(u32x4_t *)(row + (((4 * c + jg) ^ sw) << 4)) = vs[c];
-}
 
 // Scores of one 16-key tile: S^T[key][head], lane (jg, hl) getting keys
 // jg*4 + r (r = 0..3) of head hl.
-__device__ __forceinline__ f32x4_t tile_scores(const u32x4_t (&ka)[8], const bf16x8_t (&qb)[8]) {
+__device__ __forceinline__ f32x4_t tile_scores(const uint8_t *lk, const bf16x8_t (&qb)[8], int lane) {
+    const int hl = lane & 15;
+    const int jg = lane >> 4;
+    const uint8_t *krow = lk + hl * kRowBytes;
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[c]), qb[c], s, 0, 0, 0);
+    for (int c = 0; c < 8; ++c) {
+        const bf16x8_t a = *(const bf16x8_t *)(krow + (((4 * c + jg) ^ hl) << 4));
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[c], s, 0, 0, 0);
+    }
     return s;
 }
 
@@ -222,6 +246,7 @@ __device__ __forceinline__ void tile_finish(f32x4_t s, const uint8_t *lv, uint32
 
 template <int WPB, bool kSplitP>
 __global__ __launch_bounds__(64 * WPB) void qsa_prefill_kernel(const KParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_k[WPB][kNK * kRowBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_v[WPB][kNK * kRowBytes];
 
     const int lane = threadIdx.x & 63;
@@ -265,6 +290,7 @@ __global__ __launch_bounds__(64 * WPB) void qsa_prefill_kernel(const KParams p) 
         const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc((void *)irow, 0, K * 4, kRsrcFlags);
         const uint32_t row_stride = (uint32_t)p.Hkv * kRowBytes;
         const uint32_t head_off = (uint32_t)g * kRowBytes;
+        uint8_t *lk = &lds_k[w][0];
         uint8_t *lv = &lds_v[w][0];
 
         // Row byte offset of this lane's slot in tile j (kOob when masked) and
@@ -275,25 +301,25 @@ __global__ __launch_bounds__(64 * WPB) void qsa_prefill_kernel(const KParams p) 
             return ok ? (uint32_t)s * row_stride + head_off : kOob;
         };
 
-        // The loads of tile j+1 are issued right after the score MFMAs of tile
-        // j have consumed its K registers, and are in flight during the
-        // softmax and weighted-value MFMAs of tile j.
-        u32x4_t ka[8], vs[8];
+        // Tile j+1 is loaded into registers while tile j, already in LDS, is
+        // computed; the indices of tile j+2 are loaded alongside. Loads are
+        // issued even past the last tile (all slots masked there: nothing is
+        // fetched), so every iteration runs the same memory instructions.
+        u32x4_t ks[8], vs[8];
         uint32_t mask = 0, mask_next = 0;
-        int32_t inext = load_tile_idx(ri, 0, lane);
-        uint32_t off = prep(0, inext, mask);
-        load_tile_kv(rk, rv, off, ka, vs, lane);
-        inext = load_tile_idx(ri, 1, lane);
+        int32_t i0 = load_tile_idx(ri, 0, lane);
+        int32_t inext = load_tile_idx(ri, 1, lane);
+        load_tile_kv(rk, rv, prep(0, i0, mask), ks, vs, lane);
+        int32_t inext2 = load_tile_idx(ri, 2, lane);
         for (int j = 0;; ++j) {
-            store_tile_v(lv, vs, lane);
-            f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-            if (mask) sc = tile_scores(ka, qb);
-            // Issued even past the last tile (all slots masked there: nothing
-            // is fetched), so the register flow is the same in every iteration.
-            off = prep(j + 1, inext, mask_next);
-            load_tile_kv(rk, rv, off, ka, vs, lane);
-            inext = load_tile_idx(ri, j + 2, lane);
-            if (mask) tile_finish<kSplitP>(sc, lv, mask, o, st, p.scale_log2, lane);
+            store_tile_kv(lk, lv, ks, vs, lane);
+            load_tile_kv(rk, rv, prep(j + 1, inext, mask_next), ks, vs, lane);
+            inext = inext2;
+            inext2 = load_tile_idx(ri, j + 3, lane);
+            if (mask) {
+                const f32x4_t sc = tile_scores(lk, qb, lane);
+                tile_finish<kSplitP>(sc, lv, mask, o, st, p.scale_log2, lane);
+            }
             if (j + 1 >= n_tiles) break;
             mask = mask_next;
         }
