@@ -6,13 +6,14 @@
 // indexer selected for (t, KV head of h); -1 slots masked, an empty row gives
 // zero. Positions above t are masked too (causal prefill).
 //
-// Work decomposition. One wavefront owns one work item (t, g, head chunk):
+// Work decomposition. One wavefront owns one work item (g, t, head chunk):
 // the G = Hq/Hkv query heads of KV head g (at most 16 per chunk) against the K
 // selected slots of (t, g). Items are independent, so waves never synchronise
-// with each other; a block is WPB such waves. Blocks are renumbered so that
-// each XCD (block b runs on XCD b % 8) works through one contiguous range of
-// items: neighbouring query positions share their local window and sink rows
-// in that XCD's L2.
+// with each other; a block is WPB such waves. Items are numbered KV-head
+// major, and blocks are renumbered so that each XCD (block b runs on XCD
+// b % 8) works through one contiguous range of items: the waves sharing an
+// XCD's L2 hold neighbouring query positions of one KV head, whose local
+// windows, sinks and nearby picks overlap.
 //
 // Per wave, the K list is walked in tiles of 16 slots:
 //   1. one buffer load brings the tile's indices, lane l holding slot l & 15;
@@ -24,7 +25,7 @@
 //      contiguous bytes and the vector L1 sees whole-line accesses. A masked
 //      slot gets a byte offset past the end of the buffer: the range check
 //      returns zeros and nothing is fetched. The tile goes to registers, then
-//      to two swizzled LDS tiles (K and V), from which the MFMA operands are
+//      to two padded LDS tiles (K and V), from which the MFMA operands are
 //      read in their own layouts;
 //   3. S^T = K_tile . Q_g^T on v_mfma_f32_16x16x32_bf16: keys are the M side,
 //      the head group (zero-padded to 16) is N, d = 256 is the contraction.
@@ -34,20 +35,22 @@
 //      the row sums stay per lane until the epilogue. The reference max only
 //      moves when a tile max exceeds it by a slack of 2^8, so rescaling the
 //      accumulators is rare;
-//   5. O^T += V_tile^T . P^T on v_mfma_f32_16x16x16_bf16: V^T comes out of
+//   5. O^T += V_tile^T . P^T on v_mfma_f32_16x16x32_bf16: V^T comes out of
 //      LDS with ds_read_b64_tr_b16 (a 4x16 bf16 block transposed across 16
 //      lanes); P^T is already in the B-operand layout. Each weight is sent as
-//      a hi + lo pair of bf16 values (two MFMAs), so the weights carry ~16
-//      significant bits into the fp32 accumulator;
+//      a hi + lo pair of bf16 values, contracted in the same MFMA against the
+//      V values repeated along k, so the weights carry ~16 significant bits
+//      into the fp32 accumulator;
 //   6. epilogue: O / l rounded to bf16 (RNE), lse = ln 2 * (m + log2 l); an
 //      empty row writes +0.0 and -inf.
 // The loads of tile j+1 are issued right after tile j has been written to
 // LDS and are in flight while tile j is computed; indices run two tiles ahead.
 //
-// LDS bank layout. Row r of the K tile keeps 16-byte chunk c at c ^ (r & 15),
-// row r of the V tile at c ^ vswz(r). The row-contiguous stores, the K
-// operand reads (16 rows, one chunk) and the transposed V reads (4 or 8 rows,
-// 32 bytes each) then hit distinct banks in every phase.
+// LDS bank layout. K tile rows are padded to 528 bytes and V tile rows to 544:
+// the row-contiguous stores, the K operand reads (16 rows, one 16-byte chunk
+// each: row r starts 4r banks further) and the transposed V reads (4 or 8
+// rows, 32 bytes each: row r starts 8r banks further) hit distinct banks in
+// every phase, and every LDS address is a per-lane base plus an immediate.
 
 #include "qsa_internal.h"
 
@@ -61,12 +64,13 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int kD = 256;
 constexpr int kRowBytes = 512;              // one head's K or V row
 constexpr int kNK = 16;                     // selected slots per tile
+constexpr int kKStride = kRowBytes + 16;    // LDS row stride of the K tile
+constexpr int kVStride = kRowBytes + 32;    // LDS row stride of the V tile
 constexpr uint32_t kOob = 0x80000000u;      // byte offset beyond every K/V buffer
 constexpr uint32_t kRsrcFlags = 0x00020000u; // raw buffer, 32-bit data format (gfx9)
 constexpr float kLn2 = 0.693147180559945309f;
@@ -80,8 +84,8 @@ struct KParams {
     uint16_t *out;
     float *lse;
     int64_t q_pos0;
-    int32_t n_items; // T * Hkv * n_hchunks
-    int32_t Hq, Hkv, K, G, n_hchunks;
+    int32_t n_items; // Hkv * T * n_hchunks
+    int32_t T, Hq, Hkv, K, G, n_hchunks;
     uint32_t kv_bytes;  // T_kv * Hkv * 512
     float scale_log2;   // scale * log2(e)
 };
@@ -132,20 +136,16 @@ __device__ __forceinline__ void load_tile_kv(__amdgpu_buffer_rsrc_t rk, __amdgpu
     }
 }
 
-// V tile swizzle: row r keeps 16-byte chunk c at c ^ vswz(r). vswz(r) >> 1 =
-// r & 7, so the 4 (or 8) rows of a transposed-read phase read distinct
-// 32-byte slots.
-__device__ __forceinline__ int vswz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-
 __device__ __forceinline__ void store_tile_kv(uint8_t *lk, uint8_t *lv, const u32x4_t (&ks)[8],
                                               const u32x4_t (&vs)[8], int lane) {
     const int half = lane >> 5;
     const int c = lane & 31;
+    uint8_t *kb = lk + half * kKStride + c * 16;
+    uint8_t *vb = lv + half * kVStride + c * 16;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int r = 2 * i + half;
-        *(u32x4_t *)(lk + r * kRowBytes + ((c ^ (r & 15)) << 4)) = ks[i];
-        *(u32x4_t *)(lv + r * kRowBytes + ((c ^ vswz(r)) << 4)) = vs[i];
+        *(u32x4_t *)(kb + 2 * i * kKStride) = ks[i];
+        *(u32x4_t *)(vb + 2 * i * kVStride) = vs[i];
     }
 }
 
@@ -161,18 +161,22 @@ struct SoftmaxState {
 __device__ __forceinline__ f32x4_t tile_scores(const uint8_t *lk, const bf16x8_t (&qb)[8], int lane) {
     const int hl = lane & 15;
     const int jg = lane >> 4;
-    const uint8_t *krow = lk + hl * kRowBytes;
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t *krow = lk + hl * kKStride + jg * 16;
+    // two independent accumulation chains (even and odd d-chunks)
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const bf16x8_t a = *(const bf16x8_t *)(krow + (((4 * c + jg) ^ hl) << 4));
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[c], s, 0, 0, 0);
+    for (int c = 0; c < 8; c += 2) {
+        const bf16x8_t a0 = *(const bf16x8_t *)(krow + c * 64);
+        const bf16x8_t a1 = *(const bf16x8_t *)(krow + c * 64 + 64);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qb[c], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[c + 1], s1, 0, 0, 0);
     }
+    const f32x4_t s = s0 + s1;
     return s;
 }
 
 // Online softmax and weighted values of one 16-key tile whose V is in LDS.
-template <bool kSplitP>
 __device__ __forceinline__ void tile_finish(f32x4_t s, const uint8_t *lv, uint32_t mask,
                                             f32x4_t (&o)[16], SoftmaxState &st, float scale_log2,
                                             int lane) {
@@ -201,10 +205,10 @@ __device__ __forceinline__ void tile_finish(f32x4_t s, const uint8_t *lv, uint32
         for (int db = 0; db < 16; ++db) o[db] *= alpha;
     }
 
-    // Weights go to the MFMA as bf16. The output is normalised by the sum of
-    // exactly those values (a convex combination of V rows whatever the
-    // rounding); lse uses the fp32 sum. With kSplitP the weight is sent as
-    // hi + lo, two bf16 terms, and both sums agree to ~2^-17.
+    // Each weight goes to the MFMA as hi + lo, two bf16 values (~16
+    // significant bits). The output is normalised by the sum of exactly the
+    // values fed to the MFMA (a convex combination of V rows whatever the
+    // rounding); lse uses the fp32 sum.
     bf16x4_t pb;
     bf16x4_t pl;
     float psum = 0.f, esum = 0.f;
@@ -212,42 +216,35 @@ __device__ __forceinline__ void tile_finish(f32x4_t s, const uint8_t *lv, uint32
     for (int r = 0; r < 4; ++r) {
         const float pe = __builtin_amdgcn_exp2f(x[r] - st.m);
         const __bf16 hi = (__bf16)pe;
+        const __bf16 lo = (__bf16)(pe - (float)hi);
         pb[r] = hi;
+        pl[r] = lo;
         esum += pe;
-        if constexpr (kSplitP) {
-            const __bf16 lo = (__bf16)(pe - (float)hi);
-            pl[r] = lo;
-            psum += (float)hi + (float)lo;
-        } else {
-            psum += (float)hi;
-        }
+        psum += (float)hi + (float)lo;
     }
     st.l += psum;
     st.le += esum;
 
-    // V^T operand of O^T += V^T P^T (16x16x16): lane (jg, hl) addresses row
-    // jg*4 + (hl >> 2), 8 bytes at d = db*16 + (hl & 3)*4; the transposed read
-    // returns column d = db*16 + hl of rows jg*4 + 0..3.
+    // V^T operand: lane (jg, hl) addresses row jg*4 + (hl >> 2), 8 bytes at
+    // d = db*16 + (hl & 3)*4; the transposed read returns column d = db*16 + hl
+    // of rows jg*4 + 0..3. One 16x16x32 MFMA per d-block contracts both
+    // weight halves at once: the V^T values are repeated along k, the B
+    // operand carries P_hi for the first four k and P_lo for the last four.
     const int R = jg * 4 + (hl >> 2);
-    const int sw = vswz(R);
-    const uint8_t *vrow = lv + R * kRowBytes + (hl & 1) * 8;
-    const int half = (hl & 3) >> 1;
-    const i16x4_t pbi = __builtin_bit_cast(i16x4_t, pb);
-    const i16x4_t pli = __builtin_bit_cast(i16x4_t, pl);
+    const uint8_t *vrow = lv + R * kVStride + (hl & 3) * 8;
+    const bf16x8_t pp = {pb[0], pb[1], pb[2], pb[3], pl[0], pl[1], pl[2], pl[3]};
 #pragma unroll
     for (int db = 0; db < 16; ++db) {
-        const int ch = (2 * db + half) ^ sw;
-        const bf16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(vrow + (ch << 4)));
-        const i16x4_t vai = __builtin_bit_cast(i16x4_t, va);
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vai, pbi, o[db], 0, 0, 0);
-        if constexpr (kSplitP) o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vai, pli, o[db], 0, 0, 0);
+        const bf16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(vrow + db * 32));
+        const bf16x8_t vv = {va[0], va[1], va[2], va[3], va[0], va[1], va[2], va[3]};
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pp, o[db], 0, 0, 0);
     }
 }
 
-template <int WPB, bool kSplitP>
-__global__ __launch_bounds__(64 * WPB) void qsa_prefill_kernel(const KParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_k[WPB][kNK * kRowBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_v[WPB][kNK * kRowBytes];
+template <int WPB>
+__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))) void qsa_prefill_kernel(const KParams p) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_k[WPB][kNK * kKStride];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_v[WPB][kNK * kVStride];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -256,8 +253,8 @@ __global__ __launch_bounds__(64 * WPB) void qsa_prefill_kernel(const KParams p) 
 
     const int32_t hc = item % p.n_hchunks;
     const int32_t rest = item / p.n_hchunks;
-    const int32_t g = rest % p.Hkv;
-    const int32_t row = rest / p.Hkv;
+    const int32_t row = rest % p.T;
+    const int32_t g = rest / p.T;
     const int64_t tq = p.q_pos0 + row; // absolute position of this query
     const int h0 = g * p.G + hc * 16;
     const int nh = min(16, p.G - hc * 16);
@@ -318,7 +315,7 @@ __global__ __launch_bounds__(64 * WPB) void qsa_prefill_kernel(const KParams p) 
             inext2 = load_tile_idx(ri, j + 3, lane);
             if (mask) {
                 const f32x4_t sc = tile_scores(lk, qb, lane);
-                tile_finish<kSplitP>(sc, lv, mask, o, st, p.scale_log2, lane);
+                tile_finish(sc, lv, mask, o, st, p.scale_log2, lane);
             }
             if (j + 1 >= n_tiles) break;
             mask = mask_next;
@@ -343,10 +340,10 @@ __global__ __launch_bounds__(64 * WPB) void qsa_prefill_kernel(const KParams p) 
     }
 }
 
-template <int WPB, bool kSplitP>
+template <int WPB>
 qsa_status_t launch(const KParams &kp, hipStream_t stream) {
     const uint32_t blocks = (uint32_t)((kp.n_items + WPB - 1) / WPB);
-    hipLaunchKernelGGL((qsa_prefill_kernel<WPB, kSplitP>), dim3(blocks), dim3(64 * WPB), 0, stream, kp);
+    hipLaunchKernelGGL((qsa_prefill_kernel<WPB>), dim3(blocks), dim3(64 * WPB), 0, stream, kp);
     return hipGetLastError() == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH;
 }
 
@@ -361,6 +358,7 @@ qsa_status_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     kp.out = (uint16_t *)a.out;
     kp.lse = a.lse;
     kp.q_pos0 = a.q_pos0;
+    kp.T = (int32_t)a.T;
     kp.Hq = a.Hq;
     kp.Hkv = a.Hkv;
     kp.K = a.K;
@@ -371,7 +369,7 @@ qsa_status_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     kp.n_items = (int32_t)n_items;
     kp.kv_bytes = (uint32_t)(a.T_kv * a.Hkv * kRowBytes);
     kp.scale_log2 = a.scale * 1.44269504088896340736f;
-    return launch<4, true>(kp, stream);
+    return launch<4>(kp, stream);
 }
 
 } // namespace qsa
