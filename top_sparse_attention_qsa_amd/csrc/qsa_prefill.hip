@@ -31,8 +31,9 @@
 //      the head group (zero-padded to 16) is N, d = 256 is the contraction.
 //      Q lives in registers for the whole item;
 //   4. online softmax in fp32, base 2. In the S^T layout a lane holds 4 keys
-//      of one head: the row max is an in-lane max plus two cross-lane steps;
-//      the row sums stay per lane until the epilogue. The reference max only
+//      of one head: the row max is an in-lane max plus two lane-swap steps
+//      (v_permlane16_swap / v_permlane32_swap); the row sums stay per lane
+//      until the epilogue. The reference max only
 //      moves when a tile max exceeds it by a slack of 2^8, so rescaling the
 //      accumulators is rare;
 //   5. O^T += V_tile^T . P^T on v_mfma_f32_16x16x32_bf16: V^T comes out of
@@ -99,16 +100,37 @@ __device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t nb) {
     return x * q + (x < r ? x : r) + i;
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows
+// that hold one head) with the gfx950 lane-swap instructions. Swapping a value
+// with a copy of itself leaves x[l] in one register and x[l ^ 16] (or
+// x[l ^ 32]) in the other. The swap is written out as an instruction with two
+// read-write VGPR operands (no memory access) because the compiler treats the
+// two results of the builtin with equal operands as equal.
+__device__ __forceinline__ void swap_rows16(uint32_t &x, uint32_t &y) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void swap_rows32(uint32_t &x, uint32_t &y) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+
 __device__ __forceinline__ float wave_max_across_groups(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    uint32_t x = __builtin_bit_cast(uint32_t, v), y = x;
+    swap_rows16(x, y);
+    v = fmaxf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y));
+    x = __builtin_bit_cast(uint32_t, v);
+    y = x;
+    swap_rows32(x, y);
+    return fmaxf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y));
 }
 
 __device__ __forceinline__ float wave_sum_across_groups(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+    uint32_t x = __builtin_bit_cast(uint32_t, v), y = x;
+    swap_rows16(x, y);
+    v = __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+    x = __builtin_bit_cast(uint32_t, v);
+    y = x;
+    swap_rows32(x, y);
+    return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
 }
 
 // Indices of one tile: lane l reads slot j*16 + (l & 15), so every lane holds
