@@ -8,18 +8,26 @@ from .qsa_oracle import (
     D,
     attend,
     bf16_to_f64,
+    expand_blocks,
     kv_head_of,
+    pool_selected_slots,
     row_probabilities,
     selected_positions,
     sparse_prefill,
+    sparse_prefill_blocks,
+    sparse_prefill_pool,
 )
 
 __all__ = [
     "D",
     "attend",
     "bf16_to_f64",
+    "expand_blocks",
     "kv_head_of",
+    "pool_selected_slots",
     "row_probabilities",
     "selected_positions",
     "sparse_prefill",
+    "sparse_prefill_blocks",
+    "sparse_prefill_pool",
 ]

@@ -28,6 +28,19 @@ Readings taken where the pages leave a step open:
   * an empty row gives out = +0.0 and lse = -inf (log of an empty sum);
   * lse is the natural log of sum_j exp(scale * q . k_j).
 
+Two further forms of the same operation (same section "Nueve pruebas que
+pasaron", and section "Por qué QSA es la parte incómoda, en cifras" for the
+model's micro-blocks):
+  * micro-block indices: the model's indexer selects micro-blocks at a
+    compression ratio of 4; an entry b names tokens b*B .. b*B+B-1 in that
+    order, and each of them is causal-masked on its own, so the block that
+    holds the query keeps only its first (t mod B) + 1 tokens;
+  * a batch of requests over one pool of physical K/V slots (two requests may
+    share the slots of a common prefix): an entry is a slot number, the slot
+    records the position of the token it holds (negative: an empty slot), and
+    the slot is used iff it exists, holds a token, and that token's position
+    is <= the query's position in its own request.
+
 Arithmetic is float64 throughout; bf16 inputs widen to float64 exactly.
 """
 import numpy as np
@@ -120,6 +133,89 @@ def sparse_prefill(q, k, v, idx, scale: float = None, rows=None, Hq: int = None,
                 if kv_head_of(h, G) != g:
                     continue
                 o, l, _ = attend(q_t[h], k_sel, v_sel, scale)
+                out[i, h] = o
+                lse[i, h] = l
+    return out, lse
+
+
+def expand_blocks(block_row, block_size: int) -> list:
+    """Token positions named by a list of micro-block entries, in list order:
+    entry b names b*block_size, b*block_size + 1, ..., b*block_size +
+    block_size - 1. Nothing is dropped here; causality and range are applied
+    per token afterwards, exactly as for token lists."""
+    return [int(b) * block_size + i for b in block_row for i in range(block_size)]
+
+
+def sparse_prefill_blocks(q, k, v, block_idx, block_size: int, scale: float = None, rows=None,
+                          q_pos0: int = 0):
+    """Reference outputs when each index entry names a micro-block of
+    `block_size` consecutive tokens: the token operator applied to the
+    expanded lists (block_idx [T, Hkv, n_blocks] -> [T, Hkv, n_blocks *
+    block_size] token positions). Arguments otherwise as sparse_prefill."""
+    block_idx = np.asarray(block_idx)
+    R, Hkv, nb = block_idx.shape
+    tokens = np.empty((R, Hkv, nb * block_size), dtype=np.int64)
+    for i in range(R):
+        for g in range(Hkv):
+            tokens[i, g] = expand_blocks(block_idx[i, g], block_size)
+    return sparse_prefill(q, k, v, tokens, scale=scale, rows=rows, q_pos0=q_pos0,
+                          Hkv=np.asarray(k).shape[1])
+
+
+def pool_selected_slots(slot_row, q_pos: int, slot_pos) -> list:
+    """Slots a query at position q_pos (in its own request) attends to: the
+    entries s of its list that name a pool slot (0 <= s < n_slots) holding a
+    token (slot_pos[s] >= 0) at a position <= q_pos; list order, repeats kept."""
+    n_slots = len(slot_pos)
+    out = []
+    for s in slot_row:
+        s = int(s)
+        if 0 <= s < n_slots and 0 <= int(slot_pos[s]) <= q_pos:
+            out.append(s)
+    return out
+
+
+def sparse_prefill_pool(q, k_pool, v_pool, slot_idx, q_pos, slot_pos, scale: float = None, rows=None):
+    """Reference outputs of a ragged batch over a K/V slot pool.
+
+    q        [total_q, Hq, 256]  query rows of all requests, concatenated
+    k_pool, v_pool [n_slots, Hkv, 256]
+    slot_idx [total_q, Hkv, K]   pool slots (or [len(rows), Hkv, K] with rows)
+    q_pos    [total_q]           position of each query row in its request
+    slot_pos [n_slots]           position of the token held by each slot
+    rows     optional query rows to evaluate
+
+    Returns out float64 [R, Hq, 256] and lse float64 [R, Hq].
+    """
+    q = np.asarray(q)
+    k_pool = np.asarray(k_pool)
+    v_pool = np.asarray(v_pool)
+    Hq, Hkv = q.shape[1], k_pool.shape[1]
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    slot_idx = np.asarray(slot_idx)
+    q_pos = np.asarray(q_pos)
+    slot_pos = np.asarray(slot_pos)
+    if rows is None:
+        rows = np.arange(q.shape[0])
+        idx_rows = slot_idx
+    else:
+        rows = np.asarray(rows, dtype=np.int64)
+        idx_rows = slot_idx if slot_idx.shape[0] == rows.size else slot_idx[rows]
+    out = np.zeros((rows.size, Hq, D))
+    lse = np.full((rows.size, Hq), -np.inf)
+    for i, r in enumerate(rows):
+        q_r = bf16_to_f64(q[r])
+        for g in range(Hkv):
+            sel = pool_selected_slots(idx_rows[i, g], int(q_pos[r]), slot_pos)
+            k_sel = bf16_to_f64(k_pool[sel, g, :]) if sel else np.zeros((0, D))
+            v_sel = bf16_to_f64(v_pool[sel, g, :]) if sel else np.zeros((0, D))
+            for h in range(Hq):
+                if kv_head_of(h, G) != g:
+                    continue
+                o, l, _ = attend(q_r[h], k_sel, v_sel, scale)
                 out[i, h] = o
                 lse[i, h] = l
     return out, lse

@@ -21,8 +21,21 @@ Everything is NumPy on the host: arrays are returned as
   k   uint16 [T, Hkv, 256]  bf16 bit patterns
   v   uint16 [T, Hkv, 256]  bf16 bit patterns
   idx int32  [T, Hkv, K]    token positions, -1 padded
+(micro-block numbers for the block workloads). Ragged batches over a K/V slot
+pool come from `batch.make_pool_inputs`.
 """
-from .configs import CONFIGS, EXTEND_CONFIG, Config, get_config
+from .configs import (
+    ALL_CONFIGS,
+    BLOCK_CONFIGS,
+    CONFIGS,
+    EXTEND_CONFIG,
+    POOL_CONFIGS,
+    Config,
+    PoolConfig,
+    Request,
+    get_config,
+)
+from .batch import make_pool_inputs, sample_pool_rows, slot_tables
 from .generate import (
     make_inputs,
     make_qkv,
@@ -33,9 +46,17 @@ from .generate import (
 )
 
 __all__ = [
+    "ALL_CONFIGS",
+    "BLOCK_CONFIGS",
     "CONFIGS",
     "EXTEND_CONFIG",
+    "POOL_CONFIGS",
     "Config",
+    "PoolConfig",
+    "Request",
+    "make_pool_inputs",
+    "sample_pool_rows",
+    "slot_tables",
     "get_config",
     "make_inputs",
     "make_qkv",

@@ -22,6 +22,8 @@ t - 32 is never picked (taken literally).
 from dataclasses import dataclass, field
 from typing import Tuple
 
+import numpy as np
+
 D = 256
 
 
@@ -43,6 +45,7 @@ class Config:
     oracle_rows: int = 0  # 0 = all rows; otherwise sampled rows for parity checks
     q_pos0: int = 0  # absolute position of query row 0 (tokens already cached)
     T_kv: int = 0  # K/V rows; 0 means T (no cached prefix)
+    block_size: int = 1  # tokens named by one index entry (K, window, gap count entries)
     description: str = field(default="", compare=False)
 
     @property
@@ -67,8 +70,15 @@ class Config:
             "lse": (self.T, self.Hq),
         }
 
+    @property
+    def K_tokens(self) -> int:
+        """Token slots per list: K entries of block_size tokens each."""
+        return self.K * self.block_size
+
     def valid_slots(self) -> int:
-        """Number of (t, kv head, slot) entries that are valid (0 <= s <= position)."""
+        """Number of (t, kv head, token) slots that are valid (0 <= s <= position)."""
+        if self.block_size > 1:
+            return self._valid_block_slots()
         n = 0
         p0, p1, K = self.q_pos0, self.q_pos0 + self.T, self.K  # positions p0 .. p1-1
         ramp_end = min(p1, K)  # positions p < K select p + 1 slots
@@ -76,6 +86,18 @@ class Config:
             n += (ramp_end * (ramp_end + 1) - p0 * (p0 + 1)) // 2
         n += max(0, p1 - max(p0, K)) * K
         return n * self.Hkv
+
+    def _valid_block_slots(self) -> int:
+        # Row t at position p sits in block b = p // B. Rows with b + 1 <= K
+        # list every block 0..b: p + 1 valid tokens. Other rows list K blocks,
+        # one of them b itself (the window ends at b): (K - 1) * B full blocks
+        # plus the p % B + 1 tokens of b up to p.
+        assert self.window >= 1, "block lists must hold the query's own block"
+        B, K = self.block_size, self.K
+        p = self.q_pos0 + np.arange(self.T, dtype=np.int64)
+        dense = p // B + 1 <= K
+        per_row = np.where(dense, p + 1, (K - 1) * B + p % B + 1)
+        return int(per_row.sum()) * self.Hkv
 
     def gathered_bytes(self) -> int:
         """Algorithmic K+V bytes gathered: 512 B of K and 512 B of V per valid slot."""
@@ -145,15 +167,140 @@ EXTEND_CONFIG = Config(
                 "K/V cache, (12,1), K=2051: 512-token window, sink 0, uniform rest",
 )
 
-_BY_NAME = {c.name: c for c in CONFIGS + (EXTEND_CONFIG,)}
+# Micro-block selection ("Por qué QSA es la parte incómoda, en cifras": the
+# model's indexer has a compression ratio of 4 and selects 2,048 micro-blocks
+# per query). K, window and gap count blocks; the weight law of the weighted
+# sampler is 1 / (1 + (b_t - b) / 1024) in block units.
+BLOCK_CONFIGS: Tuple[Config, ...] = (
+    Config(
+        name="blocks4_t256_h3x1_nb16",
+        number=7,
+        T=256, Hq=3, Hkv=1, K=16,
+        window=4, sink=True, gap=0, sampler="uniform", block_size=4,
+        description="T=256, (3,1), 16 micro-blocks of 4 tokens: the last 4 blocks "
+                    "up to the query's own block, block 0, 11 uniform blocks",
+    ),
+    Config(
+        name="blocks4_t32768_h24x2_nb2048",
+        number=8,
+        T=32768, Hq=24, Hkv=2, K=2048,
+        window=64, sink=True, gap=0, sampler="weighted", block_size=4,
+        oracle_rows=512,
+        description="T=32768, (24,2), 2,048 micro-blocks of 4 tokens (8,192 token "
+                    "slots): 64-block window ending at the query's block, block 0, "
+                    "rest weighted 1/(1+(b_t-b)/1024), independent per KV head",
+    ),
+)
 
 
-def get_config(key) -> Config:
+@dataclass(frozen=True)
+class Request:
+    """One request of a ragged batch: `new` query tokens at positions
+    cached .. cached + new - 1. Its first `cached` tokens are already in the
+    pool: its own (share_from = -1) or the first `cached` tokens of request
+    `share_from` (a shared prefix: the same slots)."""
+    new: int
+    cached: int = 0
+    share_from: int = -1
+
+
+@dataclass(frozen=True)
+class PoolConfig:
+    """A ragged batch of requests over one K/V slot pool. Every token of every
+    request owns one slot, except shared-prefix tokens, which use the slots of
+    the request they are shared from; `free_slots` more slots hold no token.
+    Slots are assigned by a seeded random permutation (physical slots in no
+    order). Per-query index lists follow the token recipe of Config over the
+    query's own request, then name the slots of the chosen positions."""
+    name: str
+    number: int
+    requests: Tuple[Request, ...]
+    Hq: int
+    Hkv: int
+    K: int
+    window: int
+    sink: bool
+    sampler: str
+    free_slots: int = 0
+    gap: int = 0
+    scale: float = 1.0 / 16.0
+    oracle_rows: int = 0
+    description: str = field(default="", compare=False)
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def total_q(self) -> int:
+        return sum(r.new for r in self.requests)
+
+    @property
+    def T(self) -> int:  # query rows of the batch
+        return self.total_q
+
+    @property
+    def n_tokens(self) -> int:
+        """Distinct tokens held by the pool (shared prefixes counted once)."""
+        return sum(r.new + (r.cached if r.share_from < 0 else 0) for r in self.requests)
+
+    @property
+    def n_slots(self) -> int:
+        return self.n_tokens + self.free_slots
+
+    def valid_slots(self) -> int:
+        n = 0
+        for r in self.requests:
+            p = r.cached + np.arange(r.new, dtype=np.int64)
+            n += int(np.minimum(p + 1, self.K).sum())
+        return n * self.Hkv
+
+    def gathered_bytes(self) -> int:
+        return self.valid_slots() * 2 * D * 2
+
+    def useful_flops(self) -> int:
+        return self.valid_slots() * self.G * 4 * D
+
+
+# "Nueve pruebas que pasaron": physical slots in no order, two requests
+# mapping a shared prefix, cache reuse.
+POOL_CONFIGS: Tuple[PoolConfig, ...] = (
+    PoolConfig(
+        name="pool_4req_q311_h6x2_k64",
+        number=9,
+        requests=(Request(new=200), Request(new=77, cached=96, share_from=0),
+                  Request(new=33, cached=150), Request(new=1)),
+        Hq=6, Hkv=2, K=64, window=16, sink=True, sampler="uniform", free_slots=50,
+        description="4 requests (200 new; 77 new after 96 tokens shared with the first; "
+                    "33 new after 150 own cached; 1 new), (6,2), K=64, 50 empty slots",
+    ),
+    PoolConfig(
+        name="pool_4req_q32768_h24x2_k2048",
+        number=10,
+        requests=(Request(new=12288), Request(new=8192, cached=8192, share_from=0),
+                  Request(new=6144, cached=16384), Request(new=6144)),
+        Hq=24, Hkv=2, K=2048, window=256, sink=True, sampler="weighted",
+        free_slots=16384, oracle_rows=1024,
+        description="32,768 query tokens in 4 requests over a 65,536-slot pool: "
+                    "12,288 new; 8,192 new after the first 8,192 tokens of the first "
+                    "request (shared slots); 6,144 new after 16,384 own cached; "
+                    "6,144 new; 16,384 empty slots. (24,2), K=2048, 256 window, sink, "
+                    "weighted rest",
+    ),
+)
+
+ALL_CONFIGS = CONFIGS + (EXTEND_CONFIG,) + BLOCK_CONFIGS + POOL_CONFIGS
+_BY_NAME = {c.name: c for c in ALL_CONFIGS}
+_BY_NUMBER = {c.number: c for c in ALL_CONFIGS}
+assert len(_BY_NUMBER) == len(ALL_CONFIGS)
+
+
+def get_config(key):
     """Look a workload up by 1-based number, by name, or by 'c<number>'."""
-    if isinstance(key, Config):
+    if isinstance(key, (Config, PoolConfig)):
         return key
     if isinstance(key, int):
-        return EXTEND_CONFIG if key == EXTEND_CONFIG.number else CONFIGS[key - 1]
+        return _BY_NUMBER[key]
     if isinstance(key, str):
         if key in _BY_NAME:
             return _BY_NAME[key]

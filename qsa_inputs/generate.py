@@ -178,22 +178,21 @@ def _weighted_distinct(rng, tt: np.ndarray, lo: int, hi: np.ndarray, m: int) -> 
     return out
 
 
-def _idx_chunk(job):
-    (seed, c, g, T, K, window, sink, gap, sampler, q_pos0) = job
-    t0, t1 = c * CHUNK, min(T, (c + 1) * CHUNK)
-    rows = np.arange(t0, t1, dtype=np.int64) + q_pos0  # absolute positions
-    out = np.full((t1 - t0, K), -1, np.int32)
+def _position_lists(rng, pos: np.ndarray, K: int, window: int, sink: bool, gap: int,
+                    sampler: str) -> np.ndarray:
+    """Index lists [n, K] (int64, -1 padded) for queries at positions `pos`
+    (in units of the list entries: tokens, or blocks for block lists)."""
+    out = np.full((pos.size, K), -1, np.int64)
     if K == 0:
         return out
-    rng = _rng(seed, STREAM_IDX, g, c)
-    dense = rows + 1 <= K
+    dense = pos + 1 <= K
     for r in np.nonzero(dense)[0]:
-        t = rows[r]
-        out[r, : t + 1] = np.arange(t + 1, dtype=np.int32)
+        t = pos[r]
+        out[r, : t + 1] = np.arange(t + 1)
     sparse_rows = np.nonzero(~dense)[0]
     if sparse_rows.size == 0:
         return out
-    tt = rows[sparse_rows]
+    tt = pos[sparse_rows]
     lo = 1 if sink else 0
     hi = tt - window - gap
     m = K - window - (1 if sink else 0)
@@ -212,12 +211,24 @@ def _idx_chunk(job):
         parts.insert(0, np.zeros((tt.size, 1), np.int64))
     full = np.concatenate(parts, axis=1)
     full.sort(axis=1)
-    out[sparse_rows] = full.astype(np.int32)
+    out[sparse_rows] = full
     return out
 
 
+def _idx_chunk(job):
+    (seed, c, g, T, K, window, sink, gap, sampler, q_pos0, shift) = job
+    t0, t1 = c * CHUNK, min(T, (c + 1) * CHUNK)
+    # absolute positions, in entry units (block number for block lists)
+    pos = (np.arange(t0, t1, dtype=np.int64) + q_pos0) >> shift
+    rng = _rng(seed, STREAM_IDX, g, c)
+    return _position_lists(rng, pos, K, window, sink, gap, sampler).astype(np.int32)
+
+
 def make_indices(cfg: Config, seed: int = None, rows=None, workers=None) -> np.ndarray:
-    """int32 [T, Hkv, K] index lists (or [len(rows), Hkv, K] for a row subset)."""
+    """int32 [T, Hkv, K] index lists (or [len(rows), Hkv, K] for a row subset).
+
+    Entries are token positions, or micro-block numbers when the workload's
+    block_size > 1 (row t then sits in block (q_pos0 + t) // block_size)."""
     cfg = get_config(cfg)
     seed = cfg.number if seed is None else seed
     T, Hkv, K = cfg.T, cfg.Hkv, cfg.K
@@ -225,7 +236,9 @@ def make_indices(cfg: Config, seed: int = None, rows=None, workers=None) -> np.n
         raise ValueError("window + sink exceed the selection width")
     n_chunks = (T + CHUNK - 1) // CHUNK
     chunks = range(n_chunks) if rows is None else sorted(set(int(r) // CHUNK for r in rows))
-    jobs = [(seed, c, g, T, K, cfg.window, cfg.sink, cfg.gap, cfg.sampler, cfg.q_pos0)
+    shift = cfg.block_size.bit_length() - 1
+    assert cfg.block_size == 1 << shift
+    jobs = [(seed, c, g, T, K, cfg.window, cfg.sink, cfg.gap, cfg.sampler, cfg.q_pos0, shift)
             for c in chunks for g in range(Hkv)]
     parts = _map(_idx_chunk, jobs, workers)
     by_key = {(j[1], j[2]): p for j, p in zip(jobs, parts)}
