@@ -21,6 +21,11 @@ with HIP events on the stream the kernel runs on, against MI355X's 8 TB/s.
 of this same command, scaled by the counters' reading on a copy kernel of
 known size, and is reported only while the kernel source still matches the
 one the counters were taken on.
+
+Other workloads (--workload): any of the token workloads c1..c6, the
+micro-block workloads c7/c8 (entries name 4-token blocks, the model's
+compression ratio) and the ragged slot-pool batches c9/c10. Each is timed the
+same way through its own entry point.
 """
 import argparse
 import hashlib
@@ -63,17 +68,32 @@ def measured_traffic(workload: str, sha: str):
     return int(round(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]))
 
 
-def cpu_baseline(cfg, q, k, v, idx, n_rows: int):
-    """The fp64 oracle, as it is, on a seeded sample of the workload's rows."""
-    import numpy as np
-    from oracle import pool
-    from qsa_inputs import sample_rows
+def load_inputs(cfg):
+    """Host arrays of a workload: dict(q, k, v, idx[, q_pos, slot_pos])."""
+    from qsa_inputs import PoolConfig, make_indices, make_pool_inputs, make_qkv
 
-    rows = sample_rows(cfg, n=n_rows, seed=cfg.number + 1000)
+    if isinstance(cfg, PoolConfig):
+        d = make_pool_inputs(cfg)
+        return {n: d[n] for n in ("q", "k", "v", "idx", "q_pos", "slot_pos")}
+    q, k, v = make_qkv(cfg)
+    return {"q": q, "k": k, "v": v, "idx": make_indices(cfg)}
+
+
+def cpu_baseline(cfg, d, n_rows: int):
+    """The fp64 oracle, as it is, on a seeded sample of the workload's rows."""
+    from oracle import pool
+    from qsa_inputs import PoolConfig, sample_pool_rows, sample_rows
+
+    if isinstance(cfg, PoolConfig):
+        rows = sample_pool_rows(cfg, n=n_rows, seed=cfg.number + 1000)
+        kw = {"q_pos": d["q_pos"], "slot_pos": d["slot_pos"]}
+    else:
+        rows = sample_rows(cfg, n=n_rows, seed=cfg.number + 1000)
+        kw = {"q_pos0": cfg.q_pos0, "block_size": cfg.block_size if cfg.block_size > 1 else None}
     rows = rows[:n_rows]
     workers = pool.default_workers()
-    _, _, secs = pool.run_rows(q, k, v, idx[rows], rows, cfg.scale, q_pos0=cfg.q_pos0,
-                               workers=workers, return_seconds=True)
+    _, _, secs = pool.run_rows(d["q"], d["k"], d["v"], d["idx"][rows], rows, cfg.scale, workers=workers,
+                               return_seconds=True, **kw)
     return {
         "value": round(float(rows.size / secs), 3),
         "unit": "query-tokens/s",
@@ -84,12 +104,26 @@ def cpu_baseline(cfg, q, k, v, idx, n_rows: int):
     }
 
 
+def workload_config(cfg) -> dict:
+    from qsa_inputs import PoolConfig
+
+    c = {"workload": cfg.name, "T": cfg.T, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "head_dim": 256, "K": cfg.K,
+         "scale": cfg.scale}
+    if isinstance(cfg, PoolConfig):
+        c.update(requests=[{"new": r.new, "cached": r.cached, "share_from": r.share_from} for r in cfg.requests],
+                 n_slots=cfg.n_slots, free_slots=cfg.free_slots)
+    else:
+        c.update(q_pos0=cfg.q_pos0, T_kv=cfg.kv_len, block_size=cfg.block_size)
+    c.update(index_lists=cfg.description, valid_slots=cfg.valid_slots(), parallelism="single GPU")
+    return c
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c4", help="c1..c5 or a workload name (default c4)")
+    ap.add_argument("--workload", default="c4", help="c1..c10 or a workload name (default c4)")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="rows for the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -106,18 +140,17 @@ def main():
     import torch
 
     import top_sparse_attention_qsa_amd as qsa
-    from qsa_inputs import get_config, make_indices, make_qkv
+    from qsa_inputs import PoolConfig, get_config
 
     cfg = get_config(args.workload)
     t0 = time.perf_counter()
-    q, k, v = make_qkv(cfg)
-    idx = make_indices(cfg)
+    d = load_inputs(cfg)
     log(f"{cfg.name}: inputs generated in {time.perf_counter() - t0:.1f}s")
 
     cpu = None
     if not args.no_cpu_baseline and args.cpu_rows > 0:
         t0 = time.perf_counter()
-        cpu = cpu_baseline(cfg, q, k, v, idx, args.cpu_rows)
+        cpu = cpu_baseline(cfg, d, args.cpu_rows)
         log(f"cpu baseline {cpu['value']} q-tok/s on {cpu['cores']} cores ({time.perf_counter() - t0:.1f}s)")
 
     if not torch.cuda.is_available():
@@ -126,14 +159,21 @@ def main():
     dev = torch.device("cuda", 0)
     qsa.load_library()
     to_bf16 = lambda a: torch.from_numpy(a).view(torch.bfloat16).to(dev)
-    dq, dk, dv = to_bf16(q), to_bf16(k), to_bf16(v)
-    didx = torch.from_numpy(idx).to(dev)
+    dq, dk, dv = to_bf16(d["q"]), to_bf16(d["k"]), to_bf16(d["v"])
+    didx = torch.from_numpy(d["idx"]).to(dev)
     out = torch.empty((cfg.T, cfg.Hq, 256), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((cfg.T, cfg.Hq), dtype=torch.float32, device=dev)
-    del q, k, v, idx
+    if isinstance(cfg, PoolConfig):
+        dqp, dsp = torch.from_numpy(d["q_pos"]).to(dev), torch.from_numpy(d["slot_pos"]).to(dev)
+    del d
 
     def step():
-        if cfg.q_pos0:
+        if isinstance(cfg, PoolConfig):
+            qsa.sparse_prefill_pool(dq, dk, dv, didx, dqp, dsp, scale=cfg.scale, out=out, lse=lse)
+        elif cfg.block_size > 1:
+            qsa.sparse_prefill_blocks(dq, dk, dv, didx, cfg.q_pos0, cfg.block_size, scale=cfg.scale, out=out,
+                                      lse=lse)
+        elif cfg.q_pos0:
             qsa.sparse_prefill_extend(dq, dk, dv, didx, cfg.q_pos0, scale=cfg.scale, out=out, lse=lse)
         else:
             qsa.sparse_prefill(dq, dk, dv, didx, scale=cfg.scale, out=out, lse=lse)
@@ -198,14 +238,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {
-            "workload": cfg.name,
-            "T": cfg.T, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "head_dim": 256, "K": cfg.K,
-            "q_pos0": cfg.q_pos0, "T_kv": cfg.kv_len, "scale": cfg.scale,
-            "index_lists": cfg.description,
-            "valid_slots": cfg.valid_slots(),
-            "parallelism": "single GPU",
-        },
+        "config": workload_config(cfg),
         "gathered_kv_GBps": round(gathered / (ms_per_step * 1e-3) / 1e9, 1),
         "hbm_roofline_frac": round(gathered / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {

@@ -84,7 +84,7 @@ typedef enum {
  * Returns QSA_ERR_INVALID_ARG for a null pointer that would be used, T < 0,
  * T > INT32_MAX, Hq < 1, Hkv < 1, K < 0, Hq % Hkv != 0, a non-finite scale or
  * out/lse equal to an input pointer; QSA_ERR_UNSUPPORTED when
- * T * Hkv > QSA_MAX_KV_ROWS.
+ * T * Hkv > QSA_MAX_KV_ROWS or K > 2^28.
  */
 qsa_status_t qsa_sparse_prefill(const void *q, const void *k, const void *v, const int32_t *idx,
                                 int64_t T, int32_t Hq, int32_t Hkv, int32_t K, float scale,
@@ -110,11 +110,73 @@ qsa_status_t qsa_sparse_prefill_extend(const void *q, const void *k, const void 
                                        int32_t Hq, int32_t Hkv, int32_t K, float scale, void *out,
                                        float *lse, void *stream);
 
+/*
+ * qsa_sparse_prefill_blocks -- the extend operation with indices that name
+ * micro-blocks of block_size consecutive tokens instead of single tokens.
+ * "Qwen4-Exp QSA llega al Ascend de Huawei", section "Por qué QSA es la parte
+ * incómoda, en cifras", gives the model's indexer a compression ratio of 4 and
+ * a budget of 2,048 selected micro-blocks per query; section "Nueve pruebas
+ * que pasaron" tests the causal-tail remainders 0..3 at ratio 4. Entry b of a
+ * list names tokens b*block_size .. b*block_size + block_size - 1, in that
+ * order; each of those tokens s is used iff s <= q_pos0 + t (so a block that
+ * straddles the query keeps only its past part). A negative entry masks its
+ * whole block. The result equals qsa_sparse_prefill_extend on the expanded
+ * token lists (n_blocks * block_size slots, blocks in list order).
+ *
+ *   block_idx   device pointer, int32 [T, Hkv, n_blocks]
+ *   n_blocks    entries per list, >= 0
+ *   block_size  1, 2, 4, 8 or 16 (1 is qsa_sparse_prefill_extend)
+ *   others      as for qsa_sparse_prefill_extend
+ *
+ * Errors as for qsa_sparse_prefill_extend, plus QSA_ERR_INVALID_ARG for any
+ * other block_size and QSA_ERR_UNSUPPORTED for n_blocks * block_size > 2^28.
+ */
+qsa_status_t qsa_sparse_prefill_blocks(const void *q, const void *k, const void *v,
+                                       const int32_t *block_idx, int64_t T, int64_t T_kv,
+                                       int64_t q_pos0, int32_t Hq, int32_t Hkv, int32_t n_blocks,
+                                       int32_t block_size, float scale, void *out, float *lse,
+                                       void *stream);
+
+/*
+ * qsa_sparse_prefill_pool -- a ragged batch of prefill requests over one
+ * shared pool of K/V slots. "Qwen4-Exp QSA llega al Ascend de Huawei", section
+ * "Nueve pruebas que pasaron": the indices are physical slots of the KV cache,
+ * in no particular order, two requests may map a shared prefix to the same
+ * slots, and cached content is reused. Query rows of all requests are
+ * concatenated (total_q rows); each row carries its token position within its
+ * own request, and each pool slot the position of the token it holds.
+ *
+ *   q, out       bf16 [total_q, Hq, 256];  lse fp32 [total_q, Hq]
+ *   k_pool, v_pool  bf16 [n_slots, Hkv, 256]
+ *   slot_idx     int32 [total_q, Hkv, K]: pool slots chosen for the row
+ *   q_pos        int32 [total_q]: position of each query row in its request
+ *   slot_pos     int32 [n_slots]: position of the token in each slot; a
+ *                negative value marks a slot that holds no token
+ *
+ * Slot value s is used for query row r iff 0 <= s < n_slots and
+ * 0 <= slot_pos[s] <= q_pos[r]; anything else is masked, never an error. The
+ * slot lists are the indexer's and hold slots of the row's own request (the
+ * pool itself does not record which request owns a slot). For one request
+ * whose slots hold positions 0..n-1 this is qsa_sparse_prefill_extend with
+ * the same lists after mapping slots to positions.
+ *
+ * Errors: QSA_ERR_INVALID_ARG for total_q < 0, n_slots < 0, either above
+ * INT32_MAX, Hq < 1, Hkv < 1, K < 0, Hq % Hkv != 0, a non-finite scale, a
+ * null pointer that would be used (q_pos and slot_pos are used whenever
+ * total_q > 0) or out/lse equal to an input pointer; QSA_ERR_UNSUPPORTED when
+ * n_slots * Hkv > QSA_MAX_KV_ROWS or K > 2^28.
+ */
+qsa_status_t qsa_sparse_prefill_pool(const void *q, const void *k_pool, const void *v_pool,
+                                     const int32_t *slot_idx, const int32_t *q_pos,
+                                     const int32_t *slot_pos, int64_t total_q, int64_t n_slots,
+                                     int32_t Hq, int32_t Hkv, int32_t K, float scale, void *out,
+                                     float *lse, void *stream);
+
 /* Static, NUL-terminated description of a status code ("unknown status" otherwise). */
 const char *qsa_status_string(qsa_status_t status);
 
 /* ABI revision of this header; bumped on any incompatible change. */
-#define QSA_ABI_VERSION 1
+#define QSA_ABI_VERSION 2
 int32_t qsa_abi_version(void);
 
 #ifdef __cplusplus

@@ -29,8 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    assert names == ["qsa_abi_version", "qsa_sparse_prefill", "qsa_sparse_prefill_extend",
-                     "qsa_status_string"]
+    assert names == ["qsa_abi_version", "qsa_sparse_prefill", "qsa_sparse_prefill_blocks",
+                     "qsa_sparse_prefill_extend", "qsa_sparse_prefill_pool", "qsa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.qsa_abi_version() == 1
+    assert lib.qsa_abi_version() == 2
     assert lib.qsa_status_string(OK) == b"ok"
     assert lib.qsa_status_string(INVALID) == b"invalid argument"
     assert lib.qsa_status_string(UNSUPPORTED) == b"unsupported size"
@@ -95,6 +95,42 @@ def test_null_index_rejected_only_when_used(lib):
 ])
 def test_extend_argument_rules(lib, kwargs, expect):
     assert call_ext(lib, **kwargs) == expect
+
+
+def call_blk(lib, T=8, T_kv=20, p0=4, Hq=4, Hkv=2, nb=5, bs=4, scale=0.0625, idx=IDX):
+    return lib.qsa_sparse_prefill_blocks(Q, K_, V, idx, T, T_kv, p0, Hq, Hkv, nb, bs, scale, OUT, LSE, None)
+
+
+@pytest.mark.parametrize("kwargs,expect", [
+    (dict(bs=0), INVALID), (dict(bs=3), INVALID), (dict(bs=32), INVALID), (dict(bs=-4), INVALID),
+    (dict(nb=-1), INVALID), (dict(p0=-1), INVALID), (dict(T=8, T_kv=11, p0=4), INVALID),
+    (dict(idx=None), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(nb=(1 << 26) + 1, bs=4), UNSUPPORTED), (dict(nb=(1 << 24) + 1, bs=16), UNSUPPORTED),
+    (dict(T=0, nb=1 << 24, bs=16), OK), (dict(T=0, bs=16), OK), (dict(T=0, bs=5), INVALID),
+])
+def test_blocks_argument_rules(lib, kwargs, expect):
+    assert call_blk(lib, **kwargs) == expect
+
+
+QP, SP = ctypes.c_void_p(0x90000), ctypes.c_void_p(0xA0000)
+
+
+def call_pool(lib, total_q=8, n_slots=40, Hq=4, Hkv=2, K=5, scale=0.0625, q_pos=QP, slot_pos=SP, out=OUT,
+              lse=LSE, idx=IDX):
+    return lib.qsa_sparse_prefill_pool(Q, K_, V, idx, q_pos, slot_pos, total_q, n_slots, Hq, Hkv, K, scale,
+                                       out, lse, None)
+
+
+@pytest.mark.parametrize("kwargs,expect", [
+    (dict(total_q=-1), INVALID), (dict(n_slots=-1), INVALID), (dict(total_q=2 ** 31), INVALID),
+    (dict(n_slots=2 ** 31), INVALID), (dict(Hq=6, Hkv=4), INVALID), (dict(K=-2), INVALID),
+    (dict(q_pos=None), INVALID), (dict(slot_pos=None), INVALID), (dict(idx=None), INVALID),
+    (dict(out=QP), INVALID), (dict(lse=SP), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(n_slots=4194304, Hkv=1, Hq=1), UNSUPPORTED), (dict(K=(1 << 28) + 1), UNSUPPORTED),
+    (dict(total_q=0), OK), (dict(total_q=0, q_pos=None, slot_pos=None), OK),
+])
+def test_pool_argument_rules(lib, kwargs, expect):
+    assert call_pool(lib, **kwargs) == expect
 
 
 def test_python_binding_validates_before_calling():

@@ -1,0 +1,296 @@
+"""GPU parity of the micro-block and slot-pool entry points against the oracle.
+
+Micro-block lists: "Qwen4-Exp QSA llega al Ascend de Huawei" (orcarouter.ai,
+Spanish page), section "Por qué QSA es la parte incómoda, en cifras"
+(compression ratio 4, 2,048 micro-blocks per query) and section "Nueve
+pruebas que pasaron" (causal-tail remainders 0..3). Slot pools: the same
+section (unordered physical slots, two requests mapping a shared prefix,
+cache-content reuse).
+
+Besides the oracle bar (tests/parity.py), two kernel-to-kernel identities are
+checked bit for bit, since the kernel's arithmetic does not depend on where a
+row lives: a block list equals the token list it expands to, and a pool batch
+equals one extend call per request on that request's gathered cache.
+"""
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import pool as oracle_pool
+from qsa_inputs import (f32_to_bf16_bits, get_config, make_indices, make_pool_inputs, make_qkv,
+                        sample_pool_rows, sample_rows)
+from tests.parity import compare, torch_bf16_to_numpy_bits
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import top_sparse_attention_qsa_amd as qsa  # noqa: E402
+
+INT32_MIN = -(2 ** 31)
+INT32_MAX = 2 ** 31 - 1
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X: no HIP device visible")
+    qsa.load_library()
+    return torch.device("cuda", 0)
+
+
+def dev_bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to("cuda")
+
+
+def dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda")
+
+
+def rand_bf16(rng, shape):
+    return f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+
+
+def progress(msg):
+    sys.__stdout__.write(f"    {time.strftime('%H:%M:%S')} {msg}\n")
+    sys.__stdout__.flush()
+
+
+def host(out, lse):
+    torch.cuda.synchronize()
+    return torch_bf16_to_numpy_bits(out), lse.cpu().numpy()
+
+
+def run_blocks(q, k, v, bidx, B, q_pos0=0, scale=None):
+    return host(*qsa.sparse_prefill_blocks(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_i32(bidx), q_pos0, B,
+                                           scale=scale))
+
+
+def run_tokens(q, k, v, idx, q_pos0=0, scale=None):
+    return host(*qsa.sparse_prefill_extend(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_i32(idx), q_pos0,
+                                           scale=scale))
+
+
+def run_pool(q, k, v, idx, q_pos, slot_pos, scale=None):
+    return host(*qsa.sparse_prefill_pool(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_i32(idx), dev_i32(q_pos),
+                                         dev_i32(slot_pos), scale=scale))
+
+
+def expand(bidx, B):
+    """Token lists named by block lists (entries b*B .. b*B+B-1, in order);
+    values that do not fit int32 become -1 (masked either way)."""
+    t = bidx.astype(np.int64)[..., None] * B + np.arange(B)
+    t = t.reshape(bidx.shape[0], bidx.shape[1], -1)
+    t[(t > INT32_MAX) | (t < 0)] = -1
+    return t.astype(np.int32)
+
+
+# ------------------------------------------------------------------ micro-blocks
+
+
+def test_blocks_small_workload_all_rows():
+    cfg = get_config(7)
+    q, k, v = make_qkv(cfg)
+    bidx = make_indices(cfg)
+    out, lse = run_blocks(q, k, v, bidx, cfg.block_size, scale=cfg.scale)
+    ref_out, ref_lse = oracle.sparse_prefill_blocks(q, k, v, bidx, cfg.block_size, scale=cfg.scale)
+    progress(f"{cfg.name}: {compare(out, lse, ref_out, ref_lse, label=cfg.name)}")
+
+
+def test_blocks_full_size_sampled_rows():
+    cfg = get_config(8)
+    t0 = time.perf_counter()
+    q, k, v = make_qkv(cfg)
+    bidx = make_indices(cfg)
+    progress(f"{cfg.name}: inputs in {time.perf_counter() - t0:.1f}s")
+    out, lse = run_blocks(q, k, v, bidx, cfg.block_size, scale=cfg.scale)
+    rows = sample_rows(cfg)
+    progress(f"{cfg.name}: gpu done; oracle on {rows.size} rows")
+    ref_out, ref_lse = oracle_pool.run_rows(q, k, v, bidx[rows], rows, cfg.scale, block_size=cfg.block_size)
+    stats = compare(out[rows], lse[rows], ref_out, ref_lse, label=cfg.name)
+    progress(f"{cfg.name}: {stats} ({time.perf_counter() - t0:.1f}s)")
+    assert not np.any((out.view(np.uint16) & 0x7F80) == 0x7F80), "non-finite output"
+    assert np.all(np.isfinite(lse))
+    assert stats["rel_l2"] < 0.008
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 8, 16])
+def test_block_causal_tails(B):
+    """Every row lists its own block (remainders 0..B-1 all occur) among
+    random earlier blocks, a future block and -1 pads, in random order."""
+    rng = np.random.default_rng(100 + B)
+    T, Hq, Hkv, nb = 8 * B + 3, 6, 2, 11
+    q, k, v = rand_bf16(rng, (T, Hq, 256)), rand_bf16(rng, (T + B, Hkv, 256)), rand_bf16(rng, (T + B, Hkv, 256))
+    bidx = np.full((T, Hkv, nb), -1, np.int32)
+    for t in range(T):
+        bt = t // B
+        for g in range(Hkv):
+            row = [bt] + list(rng.integers(0, bt + 1, size=min(bt, 6))) + [bt + 1]
+            row = (row + [-1] * nb)[:nb]
+            rng.shuffle(row)
+            bidx[t, g] = row
+    out, lse = run_blocks(q, k[:T], v[:T], bidx, B)
+    ref_out, ref_lse = oracle.sparse_prefill_blocks(q, k[:T], v[:T], bidx, B)
+    compare(out, lse, ref_out, ref_lse, label=f"tails B={B}")
+
+
+@pytest.mark.parametrize("B", [2, 4, 16])
+def test_block_lists_equal_their_token_expansion_bitwise(B):
+    rng = np.random.default_rng(200 + B)
+    T, T_kv, p0 = 301, 420, 119
+    q, k, v = rand_bf16(rng, (T, 12, 256)), rand_bf16(rng, (T_kv, 1, 256)), rand_bf16(rng, (T_kv, 1, 256))
+    nb = 37
+    bidx = rng.integers(-3, (T_kv + B - 1) // B + 2, size=(T, 1, nb)).astype(np.int32)
+    a = run_blocks(q, k, v, bidx, B, q_pos0=p0)
+    b = run_tokens(q, k, v, expand(bidx, B), q_pos0=p0)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+    ref_out, ref_lse = oracle.sparse_prefill_blocks(q, k, v, bidx, B, q_pos0=p0)
+    compare(a[0], a[1], ref_out, ref_lse, label=f"blocks extend B={B}")
+
+
+def test_invalid_blocks_are_masked():
+    rng = np.random.default_rng(7)
+    T = 40
+    q, k, v = rand_bf16(rng, (T, 3, 256)), rand_bf16(rng, (T, 1, 256)), rand_bf16(rng, (T, 1, 256))
+    bad = np.array([-1, INT32_MIN, INT32_MAX, 1 << 29, (1 << 29) - 1, 10, -7, 1 << 30], np.int32)
+    bidx = np.broadcast_to(bad, (T, 1, bad.size)).copy()
+    bidx[:, 0, 5] = np.arange(T) // 4  # the own block, so rows are not empty
+    out, lse = run_blocks(q, k, v, bidx, 4)
+    ref_out, ref_lse = oracle.sparse_prefill_blocks(q, k, v, bidx, 4)
+    compare(out, lse, ref_out, ref_lse, label="invalid blocks")
+
+
+def test_blocks_empty_and_zero_width():
+    rng = np.random.default_rng(8)
+    q, k, v = rand_bf16(rng, (5, 2, 256)), rand_bf16(rng, (5, 1, 256)), rand_bf16(rng, (5, 1, 256))
+    out, lse = run_blocks(q, k, v, np.zeros((5, 1, 0), np.int32), 4)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+    out, lse = run_blocks(q, k, v, np.full((5, 1, 3), -1, np.int32), 4)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_block_size_is_validated():
+    rng = np.random.default_rng(9)
+    q, k = rand_bf16(rng, (4, 1, 256)), rand_bf16(rng, (4, 1, 256))
+    with pytest.raises(qsa.QsaError):
+        qsa.sparse_prefill_blocks(dev_bf16(q), dev_bf16(k), dev_bf16(k), dev_i32(np.zeros((4, 1, 2))), 0, 3)
+
+
+# ------------------------------------------------------------------ slot pool
+
+
+def _per_request_extend_bitwise(d, out, lse):
+    """Each request's rows equal one extend call over its gathered cache."""
+    k, v, idx, slot_pos = d["k"], d["v"], d["idx"], d["slot_pos"]
+    for r in d["requests"]:
+        a, b = r["rows"]
+        table = r["table"]
+        lists = idx[a:b]
+        pos = np.where(lists >= 0, slot_pos[np.maximum(lists, 0)], -1).astype(np.int32)
+        eo, el = run_tokens(d["q"][a:b], k[table], v[table], pos, q_pos0=r["cached"], scale=d["scale"])
+        np.testing.assert_array_equal(out[a:b], eo)
+        np.testing.assert_array_equal(lse[a:b], el)
+
+
+def test_pool_small_workload_all_rows():
+    d = make_pool_inputs(9)
+    out, lse = run_pool(d["q"], d["k"], d["v"], d["idx"], d["q_pos"], d["slot_pos"], scale=d["scale"])
+    ref_out, ref_lse = oracle.sparse_prefill_pool(d["q"], d["k"], d["v"], d["idx"], d["q_pos"], d["slot_pos"],
+                                                  scale=d["scale"])
+    progress(f"{d['cfg'].name}: {compare(out, lse, ref_out, ref_lse, label=d['cfg'].name)}")
+    _per_request_extend_bitwise(d, out, lse)
+
+
+def test_pool_full_size_sampled_rows():
+    t0 = time.perf_counter()
+    d = make_pool_inputs(10)
+    cfg = d["cfg"]
+    progress(f"{cfg.name}: inputs in {time.perf_counter() - t0:.1f}s")
+    args = (d["q"], d["k"], d["v"], d["idx"], d["q_pos"], d["slot_pos"])
+    out, lse = run_pool(*args, scale=cfg.scale)
+    rows = sample_pool_rows(cfg)
+    progress(f"{cfg.name}: gpu done; oracle on {rows.size} rows")
+    ref_out, ref_lse = oracle_pool.run_rows(d["q"], d["k"], d["v"], d["idx"][rows], rows, cfg.scale,
+                                            q_pos=d["q_pos"], slot_pos=d["slot_pos"])
+    stats = compare(out[rows], lse[rows], ref_out, ref_lse, label=cfg.name)
+    progress(f"{cfg.name}: {stats} ({time.perf_counter() - t0:.1f}s)")
+    assert not np.any((out.view(np.uint16) & 0x7F80) == 0x7F80), "non-finite output"
+    assert np.all(np.isfinite(lse))
+    assert stats["rel_l2"] < 0.008
+    _per_request_extend_bitwise(d, out, lse)
+    progress(f"{cfg.name}: per-request extend identical")
+
+
+def test_pool_masks_free_outside_and_future_slots():
+    """Lists of the small batch with free slots, slots past the pool, negative
+    values and the request's own later tokens written over the -1 padding."""
+    d = make_pool_inputs(9)
+    rng = np.random.default_rng(11)
+    idx = d["idx"].copy()
+    n_slots = d["slot_pos"].size
+    free = np.nonzero(d["slot_pos"] < 0)[0]
+    for r in d["requests"]:
+        a, b = r["rows"]
+        table = r["table"]
+        for i in range(a, b):
+            p = int(d["q_pos"][i])
+            for g in range(idx.shape[1]):
+                pad = np.nonzero(idx[i, g] < 0)[0]
+                junk = [int(rng.choice(free)), n_slots, n_slots + 77, INT32_MAX, INT32_MIN, -5]
+                junk += [int(s) for s in table[p + 1: p + 4]]
+                for j, s in zip(pad, junk):
+                    idx[i, g, j] = s
+    out, lse = run_pool(d["q"], d["k"], d["v"], idx, d["q_pos"], d["slot_pos"])
+    ref_out, ref_lse = oracle.sparse_prefill_pool(d["q"], d["k"], d["v"], idx, d["q_pos"], d["slot_pos"])
+    compare(out, lse, ref_out, ref_lse, label="pool masking")
+
+
+def test_pool_cache_reuse_and_inputs_unchanged():
+    """The same batch twice over the same pool buffers: identical outputs,
+    inputs untouched (cache content reused, never written)."""
+    d = make_pool_inputs(9)
+    t = [dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"]), dev_i32(d["idx"]), dev_i32(d["q_pos"]),
+         dev_i32(d["slot_pos"])]
+    before = [x.clone() for x in t]
+    o1, l1 = host(*qsa.sparse_prefill_pool(*t))
+    o2, l2 = host(*qsa.sparse_prefill_pool(*t))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    for x, y in zip(t, before):
+        assert torch.equal(x, y)
+
+
+def test_pool_edge_cases():
+    rng = np.random.default_rng(12)
+    k, v = rand_bf16(rng, (30, 2, 256)), rand_bf16(rng, (30, 2, 256))
+    slot_pos = rng.permutation(30).astype(np.int32)
+    # no query rows
+    o, l = run_pool(np.zeros((0, 4, 256), np.uint16), k, v, np.zeros((0, 2, 5), np.int32),
+                    np.zeros(0, np.int32), slot_pos)
+    assert o.shape == (0, 4, 256) and l.shape == (0, 4)
+    q = rand_bf16(rng, (6, 4, 256))
+    q_pos = np.array([0, 5, 29, -1, 100, 3], np.int32)  # a negative position sees nothing
+    idx = rng.integers(-2, 33, size=(6, 2, 9)).astype(np.int32)
+    out, lse = run_pool(q, k, v, idx, q_pos, slot_pos)
+    ref_out, ref_lse = oracle.sparse_prefill_pool(q, k, v, idx, q_pos, slot_pos)
+    compare(out, lse, ref_out, ref_lse, label="pool edge")
+    assert np.all(np.isneginf(lse[3]))
+    # zero selection width
+    out, lse = run_pool(q, k, v, np.zeros((6, 2, 0), np.int32), q_pos, slot_pos)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_pool_binding_validates():
+    rng = np.random.default_rng(13)
+    q, k = dev_bf16(rand_bf16(rng, (3, 2, 256))), dev_bf16(rand_bf16(rng, (8, 1, 256)))
+    idx = dev_i32(np.zeros((3, 1, 2)))
+    with pytest.raises(ValueError):
+        qsa.sparse_prefill_pool(q, k, k, idx, dev_i32(np.zeros(2)), dev_i32(np.zeros(8)))
+    with pytest.raises(ValueError):
+        qsa.sparse_prefill_pool(q, k, k, idx, dev_i32(np.zeros(3)), dev_i32(np.zeros(7)))
+    with pytest.raises(TypeError):
+        qsa.sparse_prefill_pool(q, k, k, idx, dev_i32(np.zeros(3)).long(), dev_i32(np.zeros(8)))

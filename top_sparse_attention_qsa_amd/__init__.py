@@ -19,6 +19,8 @@ import os
 __all__ = [
     "sparse_prefill",
     "sparse_prefill_extend",
+    "sparse_prefill_blocks",
+    "sparse_prefill_pool",
     "load_library",
     "library_path",
     "QsaError",
@@ -63,6 +65,12 @@ def load_library(path: str = None):
     lib.qsa_sparse_prefill_extend.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32,
                                               ctypes.c_float, vp, vp, vp]
     lib.qsa_sparse_prefill_extend.restype = ctypes.c_int
+    lib.qsa_sparse_prefill_blocks.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32,
+                                              ctypes.c_float, vp, vp, vp]
+    lib.qsa_sparse_prefill_blocks.restype = ctypes.c_int
+    lib.qsa_sparse_prefill_pool.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32,
+                                            ctypes.c_float, vp, vp, vp]
+    lib.qsa_sparse_prefill_pool.restype = ctypes.c_int
     lib.qsa_status_string.argtypes = [ctypes.c_int]
     lib.qsa_status_string.restype = ctypes.c_char_p
     lib.qsa_abi_version.argtypes = []
@@ -146,5 +154,51 @@ def sparse_prefill_extend(q, k, v, idx, q_pos0: int, scale=None, out=None, lse=N
     st = lib.qsa_sparse_prefill_extend(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), T,
                                        k.shape[0], int(q_pos0), Hq, Hkv, K, scale, out.data_ptr(),
                                        lse.data_ptr(), stream)
+    _check(st, lib)
+    return out, lse
+
+
+def sparse_prefill_blocks(q, k, v, block_idx, q_pos0: int, block_size: int, scale=None, out=None,
+                          lse=None):
+    """QSA sparse prefill with micro-block indices: entry b of a list names
+    tokens b*block_size .. b*block_size+block_size-1 (block_size 1, 2, 4, 8 or
+    16), each used iff its position is <= q_pos0 + t. Otherwise as
+    sparse_prefill_extend; block_idx is int32 [T, Hkv, n_blocks]."""
+    lib = load_library()
+    q, k, v, block_idx, scale, out, lse, stream = _prepare(q, k, v, block_idx, scale, out, lse)
+    T, Hq, Hkv, nb = q.shape[0], q.shape[1], k.shape[1], block_idx.shape[2]
+    st = lib.qsa_sparse_prefill_blocks(q.data_ptr(), k.data_ptr(), v.data_ptr(), block_idx.data_ptr(), T,
+                                       k.shape[0], int(q_pos0), Hq, Hkv, nb, int(block_size), scale,
+                                       out.data_ptr(), lse.data_ptr(), stream)
+    _check(st, lib)
+    return out, lse
+
+
+def sparse_prefill_pool(q, k_pool, v_pool, slot_idx, q_pos, slot_pos, scale=None, out=None, lse=None):
+    """QSA sparse prefill of a ragged batch over a shared K/V slot pool.
+
+    q [total_q, Hq, 256] bf16 (rows of all requests concatenated), k_pool /
+    v_pool [n_slots, Hkv, 256] bf16, slot_idx [total_q, Hkv, K] int32 pool
+    slots, q_pos [total_q] int32 position of each query in its request,
+    slot_pos [n_slots] int32 position of the token in each slot (negative:
+    empty slot). Slot s is used for row r iff 0 <= s < n_slots and
+    0 <= slot_pos[s] <= q_pos[r]."""
+    import torch
+
+    lib = load_library()
+    q, k_pool, v_pool, slot_idx, scale, out, lse, stream = _prepare(q, k_pool, v_pool, slot_idx, scale,
+                                                                    out, lse)
+    for name, t, n in (("q_pos", q_pos, q.shape[0]), ("slot_pos", slot_pos, k_pool.shape[0])):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32:
+            raise TypeError(f"{name} must be an int32 torch.Tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on the inputs' device")
+        if t.shape != (n,):
+            raise ValueError(f"{name} must have shape ({n},), got {tuple(t.shape)}")
+    q_pos, slot_pos = q_pos.contiguous(), slot_pos.contiguous()
+    T, Hq, Hkv, K = q.shape[0], q.shape[1], k_pool.shape[1], slot_idx.shape[2]
+    st = lib.qsa_sparse_prefill_pool(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), slot_idx.data_ptr(),
+                                     q_pos.data_ptr(), slot_pos.data_ptr(), T, k_pool.shape[0], Hq, Hkv, K,
+                                     scale, out.data_ptr(), lse.data_ptr(), stream)
     _check(st, lib)
     return out, lse

@@ -11,16 +11,20 @@ namespace qsa {
 
 // One validated call of the sparse-prefill operator.
 struct PrefillArgs {
-    const void *q;      // bf16 [T, Hq, 256]
-    const void *k;      // bf16 [T_kv, Hkv, 256]
-    const void *v;      // bf16 [T_kv, Hkv, 256]
-    const int32_t *idx; // int32 [T, Hkv, K]
-    void *out;          // bf16 [T, Hq, 256]
-    float *lse;         // fp32 [T, Hq]
-    int64_t T;          // query rows
-    int64_t T_kv;       // K/V rows
-    int64_t q_pos0;     // absolute position of query row 0
-    int32_t Hq, Hkv, K;
+    const void *q;           // bf16 [T, Hq, 256]
+    const void *k;           // bf16 [n_kv_rows, Hkv, 256]
+    const void *v;           // bf16 [n_kv_rows, Hkv, 256]
+    const int32_t *idx;      // int32 [T, Hkv, K]
+    const int32_t *q_pos;    // pool mode: int32 [T] query positions, else null
+    const int32_t *slot_pos; // pool mode: int32 [n_kv_rows] slot positions, else null
+    void *out;               // bf16 [T, Hq, 256]
+    float *lse;              // fp32 [T, Hq]
+    int64_t T;               // query rows
+    int64_t n_kv_rows;       // K/V rows: tokens of the sequence, or pool slots
+    int64_t q_pos0;          // sequence modes: absolute position of query row 0
+    int32_t Hq, Hkv;
+    int32_t K;               // entries per index list
+    int32_t blk_shift;       // an entry names 2^blk_shift tokens (0: token positions)
     float scale;
 };
 

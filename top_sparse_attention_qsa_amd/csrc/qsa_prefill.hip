@@ -82,12 +82,18 @@ struct KParams {
     const uint8_t *k;
     const uint8_t *v;
     const int32_t *idx;
+    const int32_t *q_pos;    // pool mode: position of each query row
+    const int32_t *slot_pos; // pool mode: position of the token held by each slot
     uint16_t *out;
     float *lse;
-    int64_t q_pos0;
-    int32_t n_items; // Hkv * T * n_hchunks
-    int32_t T, Hq, Hkv, K, G, n_hchunks;
-    uint32_t kv_bytes;  // T_kv * Hkv * 512
+    int64_t q_pos0;     // position of query row 0 (sequence modes)
+    int32_t n_items;    // Hkv * T * n_hchunks
+    int32_t T, Hq, Hkv, G, n_hchunks;
+    int32_t K_idx;      // entries per index list
+    int32_t K_slots;    // token slots per list: K_idx << blk_shift
+    int32_t blk_shift;  // log2 of the tokens named by one entry
+    uint32_t n_rows;    // K/V rows (tokens or pool slots)
+    uint32_t kv_bytes;  // n_rows * Hkv * 512
     float scale_log2;   // scale * log2(e)
 };
 
@@ -133,11 +139,12 @@ __device__ __forceinline__ float wave_sum_across_groups(float v) {
     return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
 }
 
-// Indices of one tile: lane l reads slot j*16 + (l & 15), so every lane holds
-// the position of the key row it will load. Slots past K read as 0 (buffer
-// range check) and are masked by position.
-__device__ __forceinline__ int32_t load_tile_idx(__amdgpu_buffer_rsrc_t ri, int j, int lane) {
-    return __builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)(j * kNK + (lane & 15)) * 4u, 0, 0);
+// Indices of one tile: lane l covers token slot j*16 + (l & 15), whose list
+// entry is (j*16 + (l & 15)) >> blk_shift (an entry names 2^blk_shift
+// consecutive tokens). Entries past the list read as 0 (buffer range check)
+// and are masked by slot number.
+__device__ __forceinline__ int32_t load_tile_idx(__amdgpu_buffer_rsrc_t ri, int j, int blk_shift, int lane) {
+    return __builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)((j * kNK + (lane & 15)) >> blk_shift) * 4u, 0, 0);
 }
 
 // K and V of one tile, row-contiguous. Instruction i covers rows 2i and
@@ -263,7 +270,12 @@ __device__ __forceinline__ void tile_finish(f32x4_t s, const uint8_t *lv, uint32
     }
 }
 
-template <int WPB>
+// kPool = false: sequence modes, entries are token positions (blk_shift 0) or
+// block numbers (an entry b names tokens b << blk_shift .. +2^blk_shift-1);
+// a token s is used iff 0 <= s <= q_pos0 + row.
+// kPool = true: entries are slots of a K/V pool; slot s is used iff
+// 0 <= s < n_rows and 0 <= slot_pos[s] <= q_pos[row].
+template <int WPB, bool kPool>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))) void qsa_prefill_kernel(const KParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_k[WPB][kNK * kKStride];
     __shared__ __attribute__((aligned(16))) uint8_t lds_v[WPB][kNK * kVStride];
@@ -277,7 +289,8 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int32_t rest = item / p.n_hchunks;
     const int32_t row = rest % p.T;
     const int32_t g = rest / p.T;
-    const int64_t tq = p.q_pos0 + row; // absolute position of this query
+    // absolute position of this query
+    const int64_t tq = kPool ? (int64_t)p.q_pos[row] : p.q_pos0 + row;
     const int h0 = g * p.G + hc * 16;
     const int nh = min(16, p.G - hc * 16);
     const int hl = lane & 15;
@@ -300,24 +313,44 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int db = 0; db < 16; ++db) o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     SoftmaxState st = {-INFINITY, 0.f, 0.f};
 
-    const int K = p.K;
-    const int n_tiles = (K + kNK - 1) / kNK;
+    const int n_tiles = (p.K_slots + kNK - 1) / kNK;
     if (n_tiles > 0) {
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)p.k, 0, (int)p.kv_bytes, kRsrcFlags);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)p.v, 0, (int)p.kv_bytes, kRsrcFlags);
-        const int32_t *irow = p.idx + ((int64_t)row * p.Hkv + g) * K;
-        const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc((void *)irow, 0, K * 4, kRsrcFlags);
+        const int32_t *irow = p.idx + ((int64_t)row * p.Hkv + g) * p.K_idx;
+        const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc((void *)irow, 0, p.K_idx * 4, kRsrcFlags);
+        __amdgpu_buffer_rsrc_t rp = ri;
+        if constexpr (kPool)
+            rp = __builtin_amdgcn_make_buffer_rsrc((void *)p.slot_pos, 0, (int)(p.n_rows * 4u), kRsrcFlags);
         const uint32_t row_stride = (uint32_t)p.Hkv * kRowBytes;
         const uint32_t head_off = (uint32_t)g * kRowBytes;
+        const int shift = p.blk_shift;
+        const int32_t sub = hl & ((1 << shift) - 1);
+        const int32_t bmax = INT32_MAX >> shift;
         uint8_t *lk = &lds_k[w][0];
         uint8_t *lv = &lds_v[w][0];
 
-        // Row byte offset of this lane's slot in tile j (kOob when masked) and
-        // the tile's validity mask (bit k = key k of the tile).
-        auto prep = [&](int j, int32_t s, uint32_t &mask) -> uint32_t {
-            const bool ok = (j * kNK + hl < K) && (s >= 0) && ((int64_t)s <= tq);
-            mask = (uint32_t)__ballot(ok) & 0xFFFFu;
-            return ok ? (uint32_t)s * row_stride + head_off : kOob;
+        // Row byte offset of this lane's slot in tile j (kOob when it cannot
+        // be used: the range check then returns zeros and fetches nothing).
+        // `ok` tells whether the slot is used; in pool mode the position test
+        // waits for the slot's position, loaded here into `spos`.
+        auto prep = [&](int j, int32_t e, bool &ok, int32_t &spos) -> uint32_t {
+            const bool in_list = j * kNK + hl < p.K_slots;
+            if constexpr (kPool) {
+                ok = in_list && e >= 0 && (uint32_t)e < p.n_rows;
+                spos = __builtin_amdgcn_raw_buffer_load_b32(rp, ok ? (uint32_t)e * 4u : kOob, 0, 0);
+                return ok ? (uint32_t)e * row_stride + head_off : kOob;
+            } else {
+                const int32_t s = (e << shift) | sub;
+                ok = in_list && e >= 0 && e <= bmax && (int64_t)s <= tq;
+                spos = 0;
+                return ok ? (uint32_t)s * row_stride + head_off : kOob;
+            }
+        };
+        // Validity mask of a tile (bit k = key k of the tile).
+        auto tile_mask = [&](bool ok, int32_t spos) -> uint32_t {
+            if constexpr (kPool) ok = ok && spos >= 0 && (int64_t)spos <= tq;
+            return (uint32_t)__ballot(ok) & 0xFFFFu;
         };
 
         // Tile j+1 is loaded into registers while tile j, already in LDS, is
@@ -325,22 +358,25 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
         // issued even past the last tile (all slots masked there: nothing is
         // fetched), so every iteration runs the same memory instructions.
         u32x4_t ks[8], vs[8];
-        uint32_t mask = 0, mask_next = 0;
-        int32_t i0 = load_tile_idx(ri, 0, lane);
-        int32_t inext = load_tile_idx(ri, 1, lane);
-        load_tile_kv(rk, rv, prep(0, i0, mask), ks, vs, lane);
-        int32_t inext2 = load_tile_idx(ri, 2, lane);
+        bool ok_cur, ok_nx;
+        int32_t sp_cur, sp_nx;
+        int32_t i0 = load_tile_idx(ri, 0, shift, lane);
+        int32_t inext = load_tile_idx(ri, 1, shift, lane);
+        load_tile_kv(rk, rv, prep(0, i0, ok_cur, sp_cur), ks, vs, lane);
+        int32_t inext2 = load_tile_idx(ri, 2, shift, lane);
         for (int j = 0;; ++j) {
             store_tile_kv(lk, lv, ks, vs, lane);
-            load_tile_kv(rk, rv, prep(j + 1, inext, mask_next), ks, vs, lane);
+            load_tile_kv(rk, rv, prep(j + 1, inext, ok_nx, sp_nx), ks, vs, lane);
             inext = inext2;
-            inext2 = load_tile_idx(ri, j + 3, lane);
+            inext2 = load_tile_idx(ri, j + 3, shift, lane);
+            const uint32_t mask = tile_mask(ok_cur, sp_cur);
             if (mask) {
                 const f32x4_t sc = tile_scores(lk, qb, lane);
                 tile_finish(sc, lv, mask, o, st, p.scale_log2, lane);
             }
             if (j + 1 >= n_tiles) break;
-            mask = mask_next;
+            ok_cur = ok_nx;
+            sp_cur = sp_nx;
         }
     }
 
@@ -362,10 +398,10 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
-template <int WPB>
+template <int WPB, bool kPool>
 qsa_status_t launch(const KParams &kp, hipStream_t stream) {
     const uint32_t blocks = (uint32_t)((kp.n_items + WPB - 1) / WPB);
-    hipLaunchKernelGGL((qsa_prefill_kernel<WPB>), dim3(blocks), dim3(64 * WPB), 0, stream, kp);
+    hipLaunchKernelGGL((qsa_prefill_kernel<WPB, kPool>), dim3(blocks), dim3(64 * WPB), 0, stream, kp);
     return hipGetLastError() == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH;
 }
 
@@ -377,21 +413,26 @@ qsa_status_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     kp.k = (const uint8_t *)a.k;
     kp.v = (const uint8_t *)a.v;
     kp.idx = a.idx;
+    kp.q_pos = a.q_pos;
+    kp.slot_pos = a.slot_pos;
     kp.out = (uint16_t *)a.out;
     kp.lse = a.lse;
     kp.q_pos0 = a.q_pos0;
     kp.T = (int32_t)a.T;
     kp.Hq = a.Hq;
     kp.Hkv = a.Hkv;
-    kp.K = a.K;
     kp.G = a.Hq / a.Hkv;
     kp.n_hchunks = (kp.G + 15) / 16;
+    kp.K_idx = a.K;
+    kp.blk_shift = a.blk_shift;
+    kp.K_slots = a.K << a.blk_shift;
     const int64_t n_items = a.T * a.Hkv * kp.n_hchunks;
-    if (n_items > INT32_MAX) return QSA_ERR_UNSUPPORTED;
+    if (n_items > INT32_MAX - 4) return QSA_ERR_UNSUPPORTED;
     kp.n_items = (int32_t)n_items;
-    kp.kv_bytes = (uint32_t)(a.T_kv * a.Hkv * kRowBytes);
+    kp.n_rows = (uint32_t)a.n_kv_rows;
+    kp.kv_bytes = (uint32_t)(a.n_kv_rows * a.Hkv * kRowBytes);
     kp.scale_log2 = a.scale * 1.44269504088896340736f;
-    return launch<4>(kp, stream);
+    return a.slot_pos ? launch<4, true>(kp, stream) : launch<4, false>(kp, stream);
 }
 
 } // namespace qsa
