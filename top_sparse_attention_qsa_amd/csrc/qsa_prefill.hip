@@ -270,12 +270,16 @@ __device__ __forceinline__ void tile_finish(f32x4_t s, const uint8_t *lv, uint32
     }
 }
 
-// kPool = false: sequence modes, entries are token positions (blk_shift 0) or
-// block numbers (an entry b names tokens b << blk_shift .. +2^blk_shift-1);
-// a token s is used iff 0 <= s <= q_pos0 + row.
-// kPool = true: entries are slots of a K/V pool; slot s is used iff
-// 0 <= s < n_rows and 0 <= slot_pos[s] <= q_pos[row].
-template <int WPB, bool kPool>
+// Index forms (kMode):
+//   kTokens  entries are token positions; a token s is used iff
+//            0 <= s <= q_pos0 + row;
+//   kBlocks  an entry b names tokens b << blk_shift .. +2^blk_shift - 1, each
+//            used under the same rule;
+//   kPool    entries are slots of a K/V pool; slot s is used iff
+//            0 <= s < n_rows and 0 <= slot_pos[s] <= q_pos[row].
+enum IndexForm { kTokens = 0, kBlocks = 1, kPool = 2 };
+
+template <int WPB, int kMode>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))) void qsa_prefill_kernel(const KParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_k[WPB][kNK * kKStride];
     __shared__ __attribute__((aligned(16))) uint8_t lds_v[WPB][kNK * kVStride];
@@ -289,8 +293,9 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int32_t rest = item / p.n_hchunks;
     const int32_t row = rest % p.T;
     const int32_t g = rest / p.T;
+    constexpr bool kIsPool = kMode == kPool;
     // absolute position of this query
-    const int64_t tq = kPool ? (int64_t)p.q_pos[row] : p.q_pos0 + row;
+    const int64_t tq = kIsPool ? (int64_t)p.q_pos[row] : p.q_pos0 + row;
     const int h0 = g * p.G + hc * 16;
     const int nh = min(16, p.G - hc * 16);
     const int hl = lane & 15;
@@ -320,37 +325,44 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int32_t *irow = p.idx + ((int64_t)row * p.Hkv + g) * p.K_idx;
         const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc((void *)irow, 0, p.K_idx * 4, kRsrcFlags);
         __amdgpu_buffer_rsrc_t rp = ri;
-        if constexpr (kPool)
+        if constexpr (kIsPool)
             rp = __builtin_amdgcn_make_buffer_rsrc((void *)p.slot_pos, 0, (int)(p.n_rows * 4u), kRsrcFlags);
         const uint32_t row_stride = (uint32_t)p.Hkv * kRowBytes;
         const uint32_t head_off = (uint32_t)g * kRowBytes;
-        const int shift = p.blk_shift;
+        const int shift = kMode == kBlocks ? p.blk_shift : 0;
         const int32_t sub = hl & ((1 << shift) - 1);
         const int32_t bmax = INT32_MAX >> shift;
         uint8_t *lk = &lds_k[w][0];
         uint8_t *lv = &lds_v[w][0];
 
         // Row byte offset of this lane's slot in tile j (kOob when it cannot
-        // be used: the range check then returns zeros and fetches nothing).
-        // `ok` tells whether the slot is used; in pool mode the position test
-        // waits for the slot's position, loaded here into `spos`.
-        auto prep = [&](int j, int32_t e, bool &ok, int32_t &spos) -> uint32_t {
+        // be used: the range check then returns zeros and fetches nothing),
+        // and what decides the tile's validity mask (bit k = key k): in the
+        // sequence forms the mask itself, taken here; in pool form the slot's
+        // token position, loaded here and tested when the tile is consumed.
+        struct Slot {
+            uint32_t mask;
+            bool ok;
+            int32_t spos;
+        };
+        auto prep = [&](int j, int32_t e, Slot &sl) -> uint32_t {
             const bool in_list = j * kNK + hl < p.K_slots;
-            if constexpr (kPool) {
-                ok = in_list && e >= 0 && (uint32_t)e < p.n_rows;
-                spos = __builtin_amdgcn_raw_buffer_load_b32(rp, ok ? (uint32_t)e * 4u : kOob, 0, 0);
-                return ok ? (uint32_t)e * row_stride + head_off : kOob;
+            if constexpr (kIsPool) {
+                sl.ok = in_list && e >= 0 && (uint32_t)e < p.n_rows;
+                sl.spos = __builtin_amdgcn_raw_buffer_load_b32(rp, sl.ok ? (uint32_t)e * 4u : kOob, 0, 0);
+                return sl.ok ? (uint32_t)e * row_stride + head_off : kOob;
             } else {
                 const int32_t s = (e << shift) | sub;
-                ok = in_list && e >= 0 && e <= bmax && (int64_t)s <= tq;
-                spos = 0;
+                const bool ok = in_list && e >= 0 && e <= bmax && (int64_t)s <= tq;
+                sl.mask = (uint32_t)__ballot(ok) & 0xFFFFu;
                 return ok ? (uint32_t)s * row_stride + head_off : kOob;
             }
         };
-        // Validity mask of a tile (bit k = key k of the tile).
-        auto tile_mask = [&](bool ok, int32_t spos) -> uint32_t {
-            if constexpr (kPool) ok = ok && spos >= 0 && (int64_t)spos <= tq;
-            return (uint32_t)__ballot(ok) & 0xFFFFu;
+        auto tile_mask = [&](const Slot &sl) -> uint32_t {
+            if constexpr (kIsPool)
+                return (uint32_t)__ballot(sl.ok && sl.spos >= 0 && (int64_t)sl.spos <= tq) & 0xFFFFu;
+            else
+                return sl.mask;
         };
 
         // Tile j+1 is loaded into registers while tile j, already in LDS, is
@@ -358,25 +370,23 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
         // issued even past the last tile (all slots masked there: nothing is
         // fetched), so every iteration runs the same memory instructions.
         u32x4_t ks[8], vs[8];
-        bool ok_cur, ok_nx;
-        int32_t sp_cur, sp_nx;
+        Slot cur, nxt;
         int32_t i0 = load_tile_idx(ri, 0, shift, lane);
         int32_t inext = load_tile_idx(ri, 1, shift, lane);
-        load_tile_kv(rk, rv, prep(0, i0, ok_cur, sp_cur), ks, vs, lane);
+        load_tile_kv(rk, rv, prep(0, i0, cur), ks, vs, lane);
         int32_t inext2 = load_tile_idx(ri, 2, shift, lane);
         for (int j = 0;; ++j) {
             store_tile_kv(lk, lv, ks, vs, lane);
-            load_tile_kv(rk, rv, prep(j + 1, inext, ok_nx, sp_nx), ks, vs, lane);
+            load_tile_kv(rk, rv, prep(j + 1, inext, nxt), ks, vs, lane);
             inext = inext2;
             inext2 = load_tile_idx(ri, j + 3, shift, lane);
-            const uint32_t mask = tile_mask(ok_cur, sp_cur);
+            const uint32_t mask = tile_mask(cur);
             if (mask) {
                 const f32x4_t sc = tile_scores(lk, qb, lane);
                 tile_finish(sc, lv, mask, o, st, p.scale_log2, lane);
             }
             if (j + 1 >= n_tiles) break;
-            ok_cur = ok_nx;
-            sp_cur = sp_nx;
+            cur = nxt;
         }
     }
 
@@ -398,10 +408,10 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
-template <int WPB, bool kPool>
+template <int WPB, int kMode>
 qsa_status_t launch(const KParams &kp, hipStream_t stream) {
     const uint32_t blocks = (uint32_t)((kp.n_items + WPB - 1) / WPB);
-    hipLaunchKernelGGL((qsa_prefill_kernel<WPB, kPool>), dim3(blocks), dim3(64 * WPB), 0, stream, kp);
+    hipLaunchKernelGGL((qsa_prefill_kernel<WPB, kMode>), dim3(blocks), dim3(64 * WPB), 0, stream, kp);
     return hipGetLastError() == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH;
 }
 
@@ -432,7 +442,8 @@ qsa_status_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     kp.n_rows = (uint32_t)a.n_kv_rows;
     kp.kv_bytes = (uint32_t)(a.n_kv_rows * a.Hkv * kRowBytes);
     kp.scale_log2 = a.scale * 1.44269504088896340736f;
-    return a.slot_pos ? launch<4, true>(kp, stream) : launch<4, false>(kp, stream);
+    if (a.slot_pos) return launch<4, kPool>(kp, stream);
+    return a.blk_shift ? launch<4, kBlocks>(kp, stream) : launch<4, kTokens>(kp, stream);
 }
 
 } // namespace qsa
