@@ -24,8 +24,9 @@ one the counters were taken on.
 
 Other workloads (--workload): any of the token workloads c1..c6, the
 micro-block workloads c7/c8 (entries name 4-token blocks, the model's
-compression ratio) and the ragged slot-pool batches c9/c10. Each is timed the
-same way through its own entry point.
+compression ratio), the ragged slot-pool batches c9/c10 and the decode
+batches c11/c12 (one query per request; the step includes the merge of the
+split lists). Each is timed the same way through its own entry point.
 """
 import argparse
 import hashlib
@@ -123,7 +124,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c4", help="c1..c10 or a workload name (default c4)")
+    ap.add_argument("--workload", default="c4", help="c1..c12 or a workload name (default c4)")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="rows for the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -167,8 +168,14 @@ def main():
         dqp, dsp = torch.from_numpy(d["q_pos"]).to(dev), torch.from_numpy(d["slot_pos"]).to(dev)
     del d
 
+    if isinstance(cfg, PoolConfig) and cfg.decode:
+        n_ws = qsa.decode_workspace_bytes(cfg.T, cfg.Hq, cfg.Hkv, cfg.K)
+        ws = torch.empty(max(n_ws, 1), dtype=torch.uint8, device=dev)
+
     def step():
-        if isinstance(cfg, PoolConfig):
+        if isinstance(cfg, PoolConfig) and cfg.decode:
+            qsa.sparse_decode(dq, dk, dv, didx, dqp, dsp, scale=cfg.scale, out=out, lse=lse, workspace=ws)
+        elif isinstance(cfg, PoolConfig):
             qsa.sparse_prefill_pool(dq, dk, dv, didx, dqp, dsp, scale=cfg.scale, out=out, lse=lse)
         elif cfg.block_size > 1:
             qsa.sparse_prefill_blocks(dq, dk, dv, didx, cfg.q_pos0, cfg.block_size, scale=cfg.scale, out=out,

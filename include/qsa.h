@@ -172,11 +172,41 @@ qsa_status_t qsa_sparse_prefill_pool(const void *q, const void *k_pool, const vo
                                      int32_t Hq, int32_t Hkv, int32_t K, float scale, void *out,
                                      float *lse, void *stream);
 
+/*
+ * qsa_sparse_decode -- one decode step of n_req requests over a K/V slot pool:
+ * the pool form above with one query row per request (row r at position
+ * q_pos[r] of request r). Decode is the serving phase the pages leave out of
+ * their prefill path ("Qwen4-Exp QSA llega al Ascend de Huawei", section "Lo
+ * que realmente añade la pull request"); the operation per row is exactly
+ * qsa_sparse_prefill_pool's, and the results agree with it to rounding.
+ *
+ * With few requests there is too little work per list to fill the GPU, so
+ * the library cuts each list into ranges of whole 16-slot tiles, computes the
+ * ranges in parallel and merges them (a fixed order: results are
+ * deterministic). The partials go to a caller-owned workspace of at least
+ * qsa_sparse_decode_workspace_bytes(n_req, Hq, Hkv, K) bytes, 16-byte
+ * aligned, device memory, overwritten by every call (calls sharing a
+ * workspace must be ordered, e.g. on one stream). When that size is 0 the
+ * workspace is not used and may be NULL.
+ *
+ *   arguments as for qsa_sparse_prefill_pool with total_q = n_req, plus
+ *   workspace, workspace_bytes
+ *
+ * Errors as for qsa_sparse_prefill_pool, plus QSA_ERR_INVALID_ARG for a
+ * workspace that is needed but NULL, smaller than required, not 16-byte
+ * aligned, or equal to another argument's pointer.
+ */
+int64_t qsa_sparse_decode_workspace_bytes(int64_t n_req, int32_t Hq, int32_t Hkv, int32_t K);
+qsa_status_t qsa_sparse_decode(const void *q, const void *k_pool, const void *v_pool, const int32_t *slot_idx,
+                               const int32_t *q_pos, const int32_t *slot_pos, int64_t n_req, int64_t n_slots,
+                               int32_t Hq, int32_t Hkv, int32_t K, float scale, void *out, float *lse,
+                               void *workspace, int64_t workspace_bytes, void *stream);
+
 /* Static, NUL-terminated description of a status code ("unknown status" otherwise). */
 const char *qsa_status_string(qsa_status_t status);
 
 /* ABI revision of this header; bumped on any incompatible change. */
-#define QSA_ABI_VERSION 2
+#define QSA_ABI_VERSION 3
 int32_t qsa_abi_version(void);
 
 #ifdef __cplusplus

@@ -28,6 +28,7 @@ from .configs import (
     ALL_CONFIGS,
     BLOCK_CONFIGS,
     CONFIGS,
+    DECODE_CONFIGS,
     EXTEND_CONFIG,
     POOL_CONFIGS,
     Config,
@@ -49,6 +50,7 @@ __all__ = [
     "ALL_CONFIGS",
     "BLOCK_CONFIGS",
     "CONFIGS",
+    "DECODE_CONFIGS",
     "EXTEND_CONFIG",
     "POOL_CONFIGS",
     "Config",

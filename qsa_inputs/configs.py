@@ -225,6 +225,7 @@ class PoolConfig:
     gap: int = 0
     scale: float = 1.0 / 16.0
     oracle_rows: int = 0
+    decode: bool = False  # one query per request, run through the decode call
     description: str = field(default="", compare=False)
 
     @property
@@ -289,7 +290,42 @@ POOL_CONFIGS: Tuple[PoolConfig, ...] = (
     ),
 )
 
-ALL_CONFIGS = CONFIGS + (EXTEND_CONFIG,) + BLOCK_CONFIGS + POOL_CONFIGS
+
+def _decode_requests(lengths, share_every):
+    """One new token per request after lengths[r] - 1 cached tokens; every
+    `share_every`-th request after the first has its whole cached prefix in
+    common with request 0 (the same slots)."""
+    reqs = []
+    for r, L in enumerate(lengths):
+        shared = r > 0 and share_every and r % share_every == 1 and L <= lengths[0]
+        reqs.append(Request(new=1, cached=L - 1, share_from=0 if shared else -1))
+    return tuple(reqs)
+
+
+# Decode: one query token per request (the serving phase the pages leave out
+# of their prefill path), lists over each request's whole context.
+DECODE_CONFIGS: Tuple[PoolConfig, ...] = (
+    PoolConfig(
+        name="decode_4req_h6x2_k512",
+        number=11,
+        requests=(Request(new=1, cached=2499), Request(new=1, cached=999, share_from=0),
+                  Request(new=1, cached=76), Request(new=1, cached=299)),
+        Hq=6, Hkv=2, K=512, window=64, sink=True, sampler="uniform", free_slots=100, decode=True,
+        description="4 requests decoding one token each after 2,499 / 999 (shared with the "
+                    "first) / 76 / 299 cached tokens, (6,2), K=512, 100 empty slots",
+    ),
+    PoolConfig(
+        name="decode_16req_ctx16k_64k_h24x2_k2048",
+        number=12,
+        requests=_decode_requests(tuple(65536 - 3276 * r for r in range(16)), share_every=4),
+        Hq=24, Hkv=2, K=2048, window=256, sink=True, sampler="weighted", free_slots=8192, decode=True,
+        description="16 requests decoding one token each, contexts 65,536 down to 16,396 "
+                    "tokens (every fourth one sharing its prefix with the first), (24,2), "
+                    "K=2048, 256 window, sink, weighted rest, 8,192 empty slots",
+    ),
+)
+
+ALL_CONFIGS = CONFIGS + (EXTEND_CONFIG,) + BLOCK_CONFIGS + POOL_CONFIGS + DECODE_CONFIGS
 _BY_NAME = {c.name: c for c in ALL_CONFIGS}
 _BY_NUMBER = {c.number: c for c in ALL_CONFIGS}
 assert len(_BY_NUMBER) == len(ALL_CONFIGS)

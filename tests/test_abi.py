@@ -29,8 +29,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    assert names == ["qsa_abi_version", "qsa_sparse_prefill", "qsa_sparse_prefill_blocks",
-                     "qsa_sparse_prefill_extend", "qsa_sparse_prefill_pool", "qsa_status_string"]
+    assert names == ["qsa_abi_version", "qsa_sparse_decode", "qsa_sparse_decode_workspace_bytes",
+                     "qsa_sparse_prefill", "qsa_sparse_prefill_blocks", "qsa_sparse_prefill_extend",
+                     "qsa_sparse_prefill_pool", "qsa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.qsa_abi_version() == 2
+    assert lib.qsa_abi_version() == 3
     assert lib.qsa_status_string(OK) == b"ok"
     assert lib.qsa_status_string(INVALID) == b"invalid argument"
     assert lib.qsa_status_string(UNSUPPORTED) == b"unsupported size"
@@ -144,3 +145,40 @@ def test_python_binding_validates_before_calling():
         qsa.sparse_prefill(q.float(), k, k, idx)
     with pytest.raises(TypeError):
         qsa.sparse_prefill(q, k, k, idx.long())
+
+
+WS = ctypes.c_void_p(0xB0000)
+
+
+def call_dec(lib, n_req=16, n_slots=1000, Hq=24, Hkv=2, K=2048, scale=0.0625, q_pos=QP, slot_pos=SP, out=OUT,
+             lse=LSE, idx=IDX, ws=WS, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = max(lib.qsa_sparse_decode_workspace_bytes(n_req, Hq, Hkv, K), 0)
+    return lib.qsa_sparse_decode(Q, K_, V, idx, q_pos, slot_pos, n_req, n_slots, Hq, Hkv, K, scale, out, lse,
+                                 ws, ws_bytes, None)
+
+
+def test_decode_workspace_sizes(lib):
+    f = lib.qsa_sparse_decode_workspace_bytes
+    # 16 requests x 2 KV heads = 32 lists of 128 tiles, cut into 16 ranges of
+    # 8 tiles: (16 * 24 heads * 16 ranges) records of 16 + 1024 bytes
+    assert f(16, 24, 2, 2048) == 16 * 24 * 16 * 1040
+    assert f(1, 24, 2, 2048) == 24 * 128 * 1040  # one tile per range
+    assert f(128, 24, 2, 2048) == 0               # 256 lists: no cut
+    assert f(127, 24, 2, 2048) == 127 * 24 * 2 * 1040
+    assert f(4, 6, 2, 16) == 0                    # one tile: nothing to cut
+    assert f(0, 24, 2, 2048) == 0
+    for bad in [(-1, 24, 2, 8), (4, 0, 2, 8), (4, 6, 4, 8), (4, 6, 2, -1), (4, 6, 2, (1 << 28) + 1)]:
+        assert f(*bad) == -1
+
+
+@pytest.mark.parametrize("kwargs,expect", [
+    (dict(n_req=-1), INVALID), (dict(q_pos=None), INVALID), (dict(slot_pos=None), INVALID),
+    (dict(ws=None), INVALID), (dict(ws_bytes=100), INVALID), (dict(ws_bytes=-1), INVALID),
+    (dict(ws=ctypes.c_void_p(0xB0008)), INVALID), (dict(ws=QP), INVALID), (dict(ws=Q), INVALID),
+    (dict(ws=OUT), INVALID), (dict(Hq=6, Hkv=4), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(n_slots=4194304, Hkv=1, Hq=1), UNSUPPORTED), (dict(n_req=0), OK),
+    (dict(n_req=0, q_pos=None, slot_pos=None, ws=None), OK),
+])
+def test_decode_argument_rules(lib, kwargs, expect):
+    assert call_dec(lib, **kwargs) == expect

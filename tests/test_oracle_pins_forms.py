@@ -311,3 +311,30 @@ def test_form_pins_catch_planted_mistakes(monkeypatch, name):
     except (IndexError, ValueError) as e:
         failures = [f"raised {type(e).__name__}"]
     assert failures != [], f"no pin caught the planted mistake {name}"
+
+
+def test_decode_batch_is_the_last_row_of_each_requests_attention():
+    """One query per request at its last position, lists naming every slot of
+    the request (plus empty slots): torch fp64 SDPA over the request's own
+    sequence, last row."""
+    rng, tables, slot_pos, k, v, _, G = _two_request_pool(20)
+    Hq = 2 * G
+    names = list(tables)
+    q = _rand_bf16(rng, (len(names), Hq, D))
+    K = 48
+    idx = np.full((len(names), 2, K), -1, np.int32)
+    q_pos = np.zeros(len(names), np.int32)
+    free = np.nonzero(slot_pos < 0)[0]
+    for r, name in enumerate(names):
+        t = tables[name]
+        row = np.array(list(t) + list(free[:3]) + [-1] * (K - t.size - 3), np.int64)
+        rng.shuffle(row)
+        idx[r] = row
+        q_pos[r] = t.size - 1
+    out, lse = oracle.sparse_prefill_pool(q, k, v, idx, q_pos, slot_pos, scale=1 / 16)
+    for r, name in enumerate(names):
+        t = tables[name]
+        allowed = np.ones((1, t.size), bool)
+        ro, rl = _sdpa_masked(q[r:r + 1], k[t], v[t], allowed, 1 / 16, G)
+        np.testing.assert_allclose(out[r:r + 1], ro, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[r:r + 1], rl, rtol=0, atol=1e-12)

@@ -294,3 +294,89 @@ def test_pool_binding_validates():
         qsa.sparse_prefill_pool(q, k, k, idx, dev_i32(np.zeros(3)), dev_i32(np.zeros(7)))
     with pytest.raises(TypeError):
         qsa.sparse_prefill_pool(q, k, k, idx, dev_i32(np.zeros(3)).long(), dev_i32(np.zeros(8)))
+
+
+# ------------------------------------------------------------------ decode
+
+
+def run_decode(q, k, v, idx, q_pos, slot_pos, scale=None, workspace=None):
+    return host(*qsa.sparse_decode(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_i32(idx), dev_i32(q_pos),
+                                   dev_i32(slot_pos), scale=scale, workspace=workspace))
+
+
+@pytest.mark.parametrize("number", [11, 12])
+def test_decode_workloads_all_rows(number):
+    t0 = time.perf_counter()
+    d = make_pool_inputs(number)
+    cfg = d["cfg"]
+    args = (d["q"], d["k"], d["v"], d["idx"], d["q_pos"], d["slot_pos"])
+    n_ws = qsa.decode_workspace_bytes(cfg.total_q, cfg.Hq, cfg.Hkv, cfg.K)
+    progress(f"{cfg.name}: inputs in {time.perf_counter() - t0:.1f}s, workspace {n_ws} B")
+    assert n_ws > 0  # these batches are small enough to be cut
+    out, lse = run_decode(*args, scale=cfg.scale)
+    rows = np.arange(cfg.total_q)
+    ref_out, ref_lse = oracle_pool.run_rows(d["q"], d["k"], d["v"], d["idx"], rows, cfg.scale, q_pos=d["q_pos"],
+                                            slot_pos=d["slot_pos"])
+    stats = compare(out, lse, ref_out, ref_lse, label=cfg.name)
+    progress(f"{cfg.name}: {stats} ({time.perf_counter() - t0:.1f}s)")
+    # the same rows through the unsplit pool kernel agree with it to rounding
+    po, pl = run_pool(*args, scale=cfg.scale)
+    compare(po, pl, ref_out, ref_lse, label=cfg.name + " pool")
+    # deterministic: a second call is identical
+    out2, lse2 = run_decode(*args, scale=cfg.scale)
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+def test_decode_sparse_and_empty_ranges():
+    """Lists of 2,051 slots with only a handful valid: most ranges of the
+    split are empty (weight 0 in the merge); one row is empty altogether and
+    one has a negative position."""
+    rng = np.random.default_rng(30)
+    n_slots, K = 5000, 2051
+    k, v = rand_bf16(rng, (n_slots, 2, 256)), rand_bf16(rng, (n_slots, 2, 256))
+    slot_pos = rng.permutation(n_slots).astype(np.int32)
+    q = rand_bf16(rng, (3, 8, 256))
+    q_pos = np.array([4000, 4999, -1], np.int32)
+    idx = np.full((3, 2, K), -1, np.int32)
+    for r in range(3):
+        for g in range(2):
+            where = rng.choice(K, size=7, replace=False)
+            idx[r, g, where] = rng.choice(n_slots, size=7, replace=False)
+    idx[1, 1, :] = -1  # KV head 1 of row 1: no slot at all
+    out, lse = run_decode(q, k, v, idx, q_pos, slot_pos)
+    ref_out, ref_lse = oracle.sparse_prefill_pool(q, k, v, idx, q_pos, slot_pos)
+    compare(out, lse, ref_out, ref_lse, label="decode sparse")
+    assert np.all(np.isneginf(lse[1, 4:])) and np.all(np.isneginf(lse[2]))
+
+
+@pytest.mark.parametrize("n_req,K", [(1, 2048), (1, 17), (3, 100), (40, 2048), (700, 64)])
+def test_decode_shapes(n_req, K):
+    rng = np.random.default_rng(n_req * 7 + K)
+    n_slots = 3000
+    k, v = rand_bf16(rng, (n_slots, 1, 256)), rand_bf16(rng, (n_slots, 1, 256))
+    slot_pos = rng.permutation(n_slots).astype(np.int32)
+    q = rand_bf16(rng, (n_req, 12, 256))
+    q_pos = rng.integers(0, n_slots, size=n_req).astype(np.int32)
+    idx = rng.integers(-5, n_slots + 5, size=(n_req, 1, K)).astype(np.int32)
+    out, lse = run_decode(q, k, v, idx, q_pos, slot_pos)
+    ref_out, ref_lse = oracle.sparse_prefill_pool(q, k, v, idx, q_pos, slot_pos)
+    compare(out, lse, ref_out, ref_lse, label=f"decode n_req={n_req} K={K}")
+
+
+def test_decode_workspace_reuse_and_checks():
+    """One workspace serves consecutive calls of different sizes; a workspace
+    below the required size is refused before anything runs."""
+    d = make_pool_inputs(11)
+    cfg = d["cfg"]
+    need = qsa.decode_workspace_bytes(cfg.total_q, cfg.Hq, cfg.Hkv, cfg.K)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    args = (d["q"], d["k"], d["v"], d["idx"], d["q_pos"], d["slot_pos"])
+    a = run_decode(*args, workspace=ws)
+    b = run_decode(*(x[:2] if i in (0, 3, 4) else x for i, x in enumerate(args)), workspace=ws)
+    fresh = run_decode(*(x[:2] if i in (0, 3, 4) else x for i, x in enumerate(args)))
+    np.testing.assert_array_equal(b[0], fresh[0])
+    np.testing.assert_array_equal(b[1], fresh[1])
+    assert a[0].shape[0] == 4
+    with pytest.raises(qsa.QsaError):
+        run_decode(*args, workspace=ws[: need - 16])

@@ -21,6 +21,8 @@ __all__ = [
     "sparse_prefill_extend",
     "sparse_prefill_blocks",
     "sparse_prefill_pool",
+    "sparse_decode",
+    "decode_workspace_bytes",
     "load_library",
     "library_path",
     "QsaError",
@@ -71,6 +73,11 @@ def load_library(path: str = None):
     lib.qsa_sparse_prefill_pool.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32,
                                             ctypes.c_float, vp, vp, vp]
     lib.qsa_sparse_prefill_pool.restype = ctypes.c_int
+    lib.qsa_sparse_decode_workspace_bytes.argtypes = [i64, i32, i32, i32]
+    lib.qsa_sparse_decode_workspace_bytes.restype = i64
+    lib.qsa_sparse_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_float, vp, vp,
+                                      vp, i64, vp]
+    lib.qsa_sparse_decode.restype = ctypes.c_int
     lib.qsa_status_string.argtypes = [ctypes.c_int]
     lib.qsa_status_string.restype = ctypes.c_char_p
     lib.qsa_abi_version.argtypes = []
@@ -174,6 +181,19 @@ def sparse_prefill_blocks(q, k, v, block_idx, q_pos0: int, block_size: int, scal
     return out, lse
 
 
+def _pool_positions(q, k_pool, q_pos, slot_pos):
+    import torch
+
+    for name, t, n in (("q_pos", q_pos, q.shape[0]), ("slot_pos", slot_pos, k_pool.shape[0])):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32:
+            raise TypeError(f"{name} must be an int32 torch.Tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on the inputs' device")
+        if t.shape != (n,):
+            raise ValueError(f"{name} must have shape ({n},), got {tuple(t.shape)}")
+    return q_pos.contiguous(), slot_pos.contiguous()
+
+
 def sparse_prefill_pool(q, k_pool, v_pool, slot_idx, q_pos, slot_pos, scale=None, out=None, lse=None):
     """QSA sparse prefill of a ragged batch over a shared K/V slot pool.
 
@@ -183,22 +203,49 @@ def sparse_prefill_pool(q, k_pool, v_pool, slot_idx, q_pos, slot_pos, scale=None
     slot_pos [n_slots] int32 position of the token in each slot (negative:
     empty slot). Slot s is used for row r iff 0 <= s < n_slots and
     0 <= slot_pos[s] <= q_pos[r]."""
+    lib = load_library()
+    q, k_pool, v_pool, slot_idx, scale, out, lse, stream = _prepare(q, k_pool, v_pool, slot_idx, scale,
+                                                                    out, lse)
+    q_pos, slot_pos = _pool_positions(q, k_pool, q_pos, slot_pos)
+    T, Hq, Hkv, K = q.shape[0], q.shape[1], k_pool.shape[1], slot_idx.shape[2]
+    st = lib.qsa_sparse_prefill_pool(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), slot_idx.data_ptr(),
+                                     q_pos.data_ptr(), slot_pos.data_ptr(), T, k_pool.shape[0], Hq, Hkv, K,
+                                     scale, out.data_ptr(), lse.data_ptr(), stream)
+    _check(st, lib)
+    return out, lse
+
+
+def decode_workspace_bytes(n_req: int, Hq: int, Hkv: int, K: int) -> int:
+    """Bytes of device workspace sparse_decode needs for these sizes (0: none)."""
+    n = load_library().qsa_sparse_decode_workspace_bytes(int(n_req), int(Hq), int(Hkv), int(K))
+    if n < 0:
+        raise ValueError("invalid sizes")
+    return int(n)
+
+
+def sparse_decode(q, k_pool, v_pool, slot_idx, q_pos, slot_pos, scale=None, out=None, lse=None, workspace=None):
+    """One decode step: one query row per request over a K/V slot pool.
+
+    Arguments as sparse_prefill_pool with q [n_req, Hq, 256]. The lists are
+    cut into ranges computed in parallel and merged; the partials go to
+    `workspace` (a uint8 device tensor of at least decode_workspace_bytes(...)
+    bytes, allocated here when None). Calls sharing a workspace must be
+    ordered on one stream."""
     import torch
 
     lib = load_library()
     q, k_pool, v_pool, slot_idx, scale, out, lse, stream = _prepare(q, k_pool, v_pool, slot_idx, scale,
                                                                     out, lse)
-    for name, t, n in (("q_pos", q_pos, q.shape[0]), ("slot_pos", slot_pos, k_pool.shape[0])):
-        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32:
-            raise TypeError(f"{name} must be an int32 torch.Tensor")
-        if t.device != q.device:
-            raise ValueError(f"{name} must be on the inputs' device")
-        if t.shape != (n,):
-            raise ValueError(f"{name} must have shape ({n},), got {tuple(t.shape)}")
-    q_pos, slot_pos = q_pos.contiguous(), slot_pos.contiguous()
-    T, Hq, Hkv, K = q.shape[0], q.shape[1], k_pool.shape[1], slot_idx.shape[2]
-    st = lib.qsa_sparse_prefill_pool(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), slot_idx.data_ptr(),
-                                     q_pos.data_ptr(), slot_pos.data_ptr(), T, k_pool.shape[0], Hq, Hkv, K,
-                                     scale, out.data_ptr(), lse.data_ptr(), stream)
+    q_pos, slot_pos = _pool_positions(q, k_pool, q_pos, slot_pos)
+    n_req, Hq, Hkv, K = q.shape[0], q.shape[1], k_pool.shape[1], slot_idx.shape[2]
+    need = decode_workspace_bytes(n_req, Hq, Hkv, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.qsa_sparse_decode(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), slot_idx.data_ptr(),
+                               q_pos.data_ptr(), slot_pos.data_ptr(), n_req, k_pool.shape[0], Hq, Hkv, K, scale,
+                               out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), ws_bytes, stream)
     _check(st, lib)
     return out, lse

@@ -64,6 +64,9 @@ qsa::PrefillArgs make_args(const void *q, const void *k, const void *v, const in
     a.K = n_entries;
     a.blk_shift = blk_shift;
     a.scale = scale;
+    a.n_splits = 1;
+    a.tiles_per_split = 0;
+    a.workspace = nullptr;
     return a;
 }
 
@@ -85,6 +88,31 @@ qsa_status_t sequence_call(const void *q, const void *k, const void *v, const in
 }
 
 } // namespace
+
+namespace qsa {
+
+SplitPlan plan_split(int64_t T, int32_t Hq, int32_t Hkv, int32_t K_slots) {
+    // Aim for about 512 waves (two per CU). More ranges fill more of the GPU
+    // but each range writes a 1 KB fp32 partial per head that the merge reads
+    // back: measured on a 16-request (24, 2) K = 2,048 decode batch, 512
+    // waves (16 ranges of 8 tiles) beat 256, 1,024, 2,048 and 4,096. Lists
+    // are only cut when the unsplit launch has fewer than 256 waves.
+    constexpr int64_t kTargetWaves = 512;
+    const int64_t n_tiles = ((int64_t)K_slots + 15) / 16;
+    const int64_t items = T * Hkv * ((Hq / Hkv + 15) / 16);
+    if (n_tiles <= 1 || items >= kTargetWaves / 2) return {1, (int32_t)n_tiles};
+    int64_t tps = (n_tiles * items + kTargetWaves - 1) / kTargetWaves;
+    if (tps < 1) tps = 1;
+    return {(int32_t)((n_tiles + tps - 1) / tps), (int32_t)tps};
+}
+
+int64_t split_workspace_bytes(int64_t T, int32_t Hq, const SplitPlan &plan) {
+    if (plan.n_splits <= 1) return 0;
+    // per (row, head, range): a 16-byte (m, l, le) record and 256 fp32 of O
+    return T * Hq * plan.n_splits * (16 + 256 * 4);
+}
+
+} // namespace qsa
 
 extern "C" {
 
@@ -124,6 +152,38 @@ qsa_status_t qsa_sparse_prefill_pool(const void *q, const void *k_pool, const vo
         make_args(q, k_pool, v_pool, slot_idx, total_q, n_slots, 0, Hq, Hkv, K, 0, scale, out, lse);
     a.q_pos = q_pos;
     a.slot_pos = slot_pos;
+    return run(a, stream);
+}
+
+int64_t qsa_sparse_decode_workspace_bytes(int64_t n_req, int32_t Hq, int32_t Hkv, int32_t K) {
+    if (n_req < 0 || n_req > INT32_MAX || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || K < 0 || K > kMaxK) return -1;
+    return qsa::split_workspace_bytes(n_req, Hq, qsa::plan_split(n_req, Hq, Hkv, K));
+}
+
+qsa_status_t qsa_sparse_decode(const void *q, const void *k_pool, const void *v_pool, const int32_t *slot_idx,
+                               const int32_t *q_pos, const int32_t *slot_pos, int64_t n_req, int64_t n_slots,
+                               int32_t Hq, int32_t Hkv, int32_t K, float scale, void *out, float *lse,
+                               void *workspace, int64_t workspace_bytes, void *stream) {
+    const qsa_status_t st =
+        check_common(q, k_pool, v_pool, slot_idx, n_req, n_slots, Hq, Hkv, K, 0, scale, out, lse);
+    if (st != QSA_OK || n_req == 0) return st;
+    if (q_pos == nullptr || slot_pos == nullptr || workspace_bytes < 0) return QSA_ERR_INVALID_ARG;
+    if (aliases(out, lse, {(const void *)q_pos, (const void *)slot_pos, workspace})) return QSA_ERR_INVALID_ARG;
+    const qsa::SplitPlan plan = qsa::plan_split(n_req, Hq, Hkv, K);
+    const int64_t need = qsa::split_workspace_bytes(n_req, Hq, plan);
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 15u) != 0)
+            return QSA_ERR_INVALID_ARG;
+        for (const void *in : {q, k_pool, v_pool, (const void *)slot_idx, (const void *)q_pos,
+                               (const void *)slot_pos})
+            if (in == workspace) return QSA_ERR_INVALID_ARG;
+    }
+    qsa::PrefillArgs a = make_args(q, k_pool, v_pool, slot_idx, n_req, n_slots, 0, Hq, Hkv, K, 0, scale, out, lse);
+    a.q_pos = q_pos;
+    a.slot_pos = slot_pos;
+    a.n_splits = plan.n_splits;
+    a.tiles_per_split = plan.tiles_per_split;
+    a.workspace = need > 0 ? workspace : nullptr;
     return run(a, stream);
 }
 

@@ -26,7 +26,22 @@ struct PrefillArgs {
     int32_t K;               // entries per index list
     int32_t blk_shift;       // an entry names 2^blk_shift tokens (0: token positions)
     float scale;
+    int32_t n_splits;        // pool form: ranges each list is cut into (1: none)
+    int32_t tiles_per_split; // 16-slot tiles per range
+    void *workspace;         // n_splits > 1: split_workspace_bytes(...) bytes, 16-byte aligned
 };
+
+// How a list of K_slots slots is cut for T query rows so that the launch
+// fills the GPU: every range holds tiles_per_split whole 16-slot tiles (the
+// last may hold fewer), n_splits ranges in all.
+struct SplitPlan {
+    int32_t n_splits;
+    int32_t tiles_per_split;
+};
+SplitPlan plan_split(int64_t T, int32_t Hq, int32_t Hkv, int32_t K_slots);
+
+// Workspace bytes of a split launch (0 when n_splits == 1).
+int64_t split_workspace_bytes(int64_t T, int32_t Hq, const SplitPlan &plan);
 
 // Enqueue the operator on `stream`. Arguments are already validated and T > 0.
 qsa_status_t launch_prefill(const PrefillArgs &a, hipStream_t stream);

@@ -47,6 +47,14 @@
 // The loads of tile j+1 are issued right after tile j has been written to
 // LDS and are in flight while tile j is computed; indices run two tiles ahead.
 //
+// Split lists (decode). With one query per request there are too few items
+// to fill the chip, so each item's list can be cut into n_splits ranges of
+// whole tiles, one wave per range. Such a wave writes its unnormalised fp32
+// O, its reference max m and its two weight sums to a workspace instead of
+// the epilogue, and qsa_combine_kernel merges the ranges of each (row, head):
+// with M = max m_s, O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, and lse
+// from the fp32 sums likewise.
+//
 // LDS bank layout. K tile rows are padded to 528 bytes and V tile rows to 544:
 // the row-contiguous stores, the K operand reads (16 rows, one 16-byte chunk
 // each: row r starts 4r banks further) and the transposed V reads (4 or 8
@@ -95,6 +103,10 @@ struct KParams {
     uint32_t n_rows;    // K/V rows (tokens or pool slots)
     uint32_t kv_bytes;  // n_rows * Hkv * 512
     float scale_log2;   // scale * log2(e)
+    int32_t n_splits;        // ranges per list (1: no split)
+    int32_t tiles_per_split; // tiles per range
+    float *ws_o;             // split: fp32 [T, Hq, n_splits, 256] partial O
+    f32x4_t *ws_ml;          // split: [T, Hq, n_splits] (m, l, le, 0)
 };
 
 // Blocks are dealt round-robin over the 8 XCDs (block b runs on XCD b % 8).
@@ -279,7 +291,7 @@ __device__ __forceinline__ void tile_finish(f32x4_t s, const uint8_t *lv, uint32
 //            0 <= s < n_rows and 0 <= slot_pos[s] <= q_pos[row].
 enum IndexForm { kTokens = 0, kBlocks = 1, kPool = 2 };
 
-template <int WPB, int kMode>
+template <int WPB, int kMode, bool kSplit>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))) void qsa_prefill_kernel(const KParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_k[WPB][kNK * kKStride];
     __shared__ __attribute__((aligned(16))) uint8_t lds_v[WPB][kNK * kVStride];
@@ -289,8 +301,10 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int32_t item = (int32_t)xcd_contiguous(blockIdx.x, gridDim.x) * WPB + w;
     if (item >= p.n_items) return;
 
-    const int32_t hc = item % p.n_hchunks;
-    const int32_t rest = item / p.n_hchunks;
+    const int32_t sp = kSplit ? item % p.n_splits : 0;
+    const int32_t item_h = kSplit ? item / p.n_splits : item;
+    const int32_t hc = item_h % p.n_hchunks;
+    const int32_t rest = item_h / p.n_hchunks;
     const int32_t row = rest % p.T;
     const int32_t g = rest / p.T;
     constexpr bool kIsPool = kMode == kPool;
@@ -318,8 +332,12 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int db = 0; db < 16; ++db) o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     SoftmaxState st = {-INFINITY, 0.f, 0.f};
 
-    const int n_tiles = (p.K_slots + kNK - 1) / kNK;
-    if (n_tiles > 0) {
+    // this wave's tiles: [j_begin, j_end) of the list
+    const int n_list_tiles = (p.K_slots + kNK - 1) / kNK;
+    const int j_begin = kSplit ? sp * p.tiles_per_split : 0;
+    const int j_end = kSplit ? min(n_list_tiles, j_begin + p.tiles_per_split) : n_list_tiles;
+    const int32_t slot_end = min(p.K_slots, j_end * kNK);
+    if (j_end > j_begin) {
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)p.k, 0, (int)p.kv_bytes, kRsrcFlags);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)p.v, 0, (int)p.kv_bytes, kRsrcFlags);
         const int32_t *irow = p.idx + ((int64_t)row * p.Hkv + g) * p.K_idx;
@@ -346,7 +364,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
             int32_t spos;
         };
         auto prep = [&](int j, int32_t e, Slot &sl) -> uint32_t {
-            const bool in_list = j * kNK + hl < p.K_slots;
+            const bool in_list = j * kNK + hl < slot_end;
             if constexpr (kIsPool) {
                 sl.ok = in_list && e >= 0 && (uint32_t)e < p.n_rows;
                 sl.spos = __builtin_amdgcn_raw_buffer_load_b32(rp, sl.ok ? (uint32_t)e * 4u : kOob, 0, 0);
@@ -371,11 +389,11 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
         // fetched), so every iteration runs the same memory instructions.
         u32x4_t ks[8], vs[8];
         Slot cur, nxt;
-        int32_t i0 = load_tile_idx(ri, 0, shift, lane);
-        int32_t inext = load_tile_idx(ri, 1, shift, lane);
-        load_tile_kv(rk, rv, prep(0, i0, cur), ks, vs, lane);
-        int32_t inext2 = load_tile_idx(ri, 2, shift, lane);
-        for (int j = 0;; ++j) {
+        int32_t i0 = load_tile_idx(ri, j_begin, shift, lane);
+        int32_t inext = load_tile_idx(ri, j_begin + 1, shift, lane);
+        load_tile_kv(rk, rv, prep(j_begin, i0, cur), ks, vs, lane);
+        int32_t inext2 = load_tile_idx(ri, j_begin + 2, shift, lane);
+        for (int j = j_begin;; ++j) {
             store_tile_kv(lk, lv, ks, vs, lane);
             load_tile_kv(rk, rv, prep(j + 1, inext, nxt), ks, vs, lane);
             inext = inext2;
@@ -385,13 +403,25 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
                 const f32x4_t sc = tile_scores(lk, qb, lane);
                 tile_finish(sc, lv, mask, o, st, p.scale_log2, lane);
             }
-            if (j + 1 >= n_tiles) break;
+            if (j + 1 >= j_end) break;
             cur = nxt;
         }
     }
 
     const float l_tot = wave_sum_across_groups(st.l);
     const float le_tot = wave_sum_across_groups(st.le);
+    if constexpr (kSplit) {
+        // partial of range sp: O relative to 2^m, lane (jg, hl) holding
+        // d = db*16 + jg*4 + r of head h0 + hl
+        if (hl < nh) {
+            const int64_t prow = ((int64_t)row * p.Hq + h0 + hl) * p.n_splits + sp;
+            float *wo = p.ws_o + prow * kD + jg * 4;
+#pragma unroll
+            for (int db = 0; db < 16; ++db) *(f32x4_t *)(wo + db * 16) = o[db];
+            if (jg == 0) p.ws_ml[prow] = (f32x4_t){st.m, l_tot, le_tot, 0.f};
+        }
+        return;
+    }
     if (hl < nh) {
         const int64_t orow = (int64_t)row * p.Hq + h0 + hl;
         uint16_t *optr = p.out + orow * kD + jg * 4;
@@ -408,11 +438,90 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
-template <int WPB, int kMode>
+// Full-wave reductions for the merge kernel (six butterfly steps of lane
+// shuffles; the merge is small and off the gather's critical path).
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum64(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Merge of the n_splits partials of each (row, head): one wave per pair.
+// The (m, l, le) records are spread over the lanes for the max and the two
+// sums; then lane l accumulates d = 4l .. 4l+3 over the ranges, eight partial
+// rows in flight at a time. A range with no valid key has m = -inf and weight
+// 0; a row with none at all gets +0.0 and lse = -inf.
+template <int WPB>
+__global__ __launch_bounds__(64 * WPB) void qsa_combine_kernel(const float *__restrict__ ws_o,
+                                                               const f32x4_t *__restrict__ ws_ml,
+                                                               uint16_t *__restrict__ out, float *__restrict__ lse,
+                                                               int32_t n_pairs, int32_t n_splits) {
+    const int lane = threadIdx.x & 63;
+    const int32_t pair = (int32_t)blockIdx.x * WPB + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (pair >= n_pairs) return;
+    const f32x4_t *ml = ws_ml + (int64_t)pair * n_splits;
+    const float *po = ws_o + (int64_t)pair * n_splits * kD + lane * 4;
+
+    float mloc = -INFINITY;
+    for (int s = lane; s < n_splits; s += 64) mloc = fmaxf(mloc, ml[s][0]);
+    const float M = wave_max64(mloc);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f, LE = 0.f;
+    if (M != -INFINITY) {
+        float lloc = 0.f, leloc = 0.f;
+        for (int s = lane; s < n_splits; s += 64) {
+            const f32x4_t m = ml[s];
+            const float w = m[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[0] - M);
+            lloc += w * m[1];
+            leloc += w * m[2];
+        }
+        L = wave_sum64(lloc);
+        LE = wave_sum64(leloc);
+        int s = 0;
+        for (; s + 8 <= n_splits; s += 8) {
+            f32x4_t part[8];
+            float w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                part[u] = *(const f32x4_t *)(po + (int64_t)(s + u) * kD);
+                const float m = ml[s + u][0];
+                w[u] = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += w[u] * part[u];
+        }
+        for (; s < n_splits; ++s) {
+            const float m = ml[s][0];
+            const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+            acc += w * *(const f32x4_t *)(po + (int64_t)s * kD);
+        }
+    }
+    const bool empty = !(L > 0.f);
+    const float inv = empty ? 0.f : 1.0f / L;
+    bf16x4_t r4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) r4[r] = (__bf16)(acc[r] * inv);
+    *(bf16x4_t *)(out + (int64_t)pair * kD + lane * 4) = r4;
+    if (lane == 0) lse[pair] = empty ? -INFINITY : (M + __log2f(LE)) * kLn2;
+}
+
+template <int WPB, int kMode, bool kSplit>
 qsa_status_t launch(const KParams &kp, hipStream_t stream) {
     const uint32_t blocks = (uint32_t)((kp.n_items + WPB - 1) / WPB);
-    hipLaunchKernelGGL((qsa_prefill_kernel<WPB, kMode>), dim3(blocks), dim3(64 * WPB), 0, stream, kp);
-    return hipGetLastError() == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH;
+    hipLaunchKernelGGL((qsa_prefill_kernel<WPB, kMode, kSplit>), dim3(blocks), dim3(64 * WPB), 0, stream, kp);
+    if (hipGetLastError() != hipSuccess) return QSA_ERR_LAUNCH;
+    if constexpr (kSplit) {
+        const int32_t n_pairs = kp.T * kp.Hq;
+        hipLaunchKernelGGL((qsa_combine_kernel<4>), dim3((uint32_t)((n_pairs + 3) / 4)), dim3(256), 0, stream,
+                           (const float *)kp.ws_o, (const f32x4_t *)kp.ws_ml, kp.out, kp.lse, n_pairs, kp.n_splits);
+        if (hipGetLastError() != hipSuccess) return QSA_ERR_LAUNCH;
+    }
+    return QSA_OK;
 }
 
 } // namespace
@@ -442,8 +551,25 @@ qsa_status_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     kp.n_rows = (uint32_t)a.n_kv_rows;
     kp.kv_bytes = (uint32_t)(a.n_kv_rows * a.Hkv * kRowBytes);
     kp.scale_log2 = a.scale * 1.44269504088896340736f;
-    if (a.slot_pos) return launch<4, kPool>(kp, stream);
-    return a.blk_shift ? launch<4, kBlocks>(kp, stream) : launch<4, kTokens>(kp, stream);
+    kp.n_splits = 1;
+    kp.tiles_per_split = 0;
+    kp.ws_o = nullptr;
+    kp.ws_ml = nullptr;
+    if (a.n_splits > 1) {
+        // pool form only (decode); workspace: [pairs * n_splits] (m, l, le, 0)
+        // records, then [pairs * n_splits * 256] fp32 partial O
+        if (!a.slot_pos || a.workspace == nullptr) return QSA_ERR_INVALID_ARG;
+        const int64_t split_items = n_items * a.n_splits;
+        if (split_items > INT32_MAX - 4) return QSA_ERR_UNSUPPORTED;
+        kp.n_items = (int32_t)split_items;
+        kp.n_splits = a.n_splits;
+        kp.tiles_per_split = a.tiles_per_split;
+        kp.ws_ml = (f32x4_t *)a.workspace;
+        kp.ws_o = (float *)((f32x4_t *)a.workspace + a.T * a.Hq * a.n_splits);
+        return launch<4, kPool, true>(kp, stream);
+    }
+    if (a.slot_pos) return launch<4, kPool, false>(kp, stream);
+    return a.blk_shift ? launch<4, kBlocks, false>(kp, stream) : launch<4, kTokens, false>(kp, stream);
 }
 
 } // namespace qsa
