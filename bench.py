@@ -125,7 +125,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4", help="c1..c12 or a workload name (default c4)")
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="rows for the oracle CPU baseline")
+    ap.add_argument("--cpu-rows", type=int, default=24576,
+                    help="rows for the oracle CPU baseline (about 10 s on 16 cores for the default workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 

@@ -22,11 +22,12 @@
 //   2. the 16 K rows and 16 V rows (512 B each) are gathered row-contiguously:
 //      each 16-byte load instruction covers two whole rows, lane l reading
 //      chunk l & 31 of row 2i + (l >> 5), so every quad of lanes reads 64
-//      contiguous bytes and the vector L1 sees whole-line accesses. A masked
-//      slot gets a byte offset past the end of the buffer: the range check
-//      returns zeros and nothing is fetched. The tile goes to registers, then
-//      to two padded LDS tiles (K and V), from which the MFMA operands are
-//      read in their own layouts;
+//      contiguous bytes and the vector L1 sees whole-line accesses (the row
+//      offsets reach the lanes by DPP row broadcasts). A masked slot gets a
+//      byte offset past the end of the buffer: the range check returns zeros
+//      and nothing is fetched. The tile goes to registers, then to two padded
+//      LDS tiles (K and V), from which the MFMA operands are read in their
+//      own layouts;
 //   3. S^T = K_tile . Q_g^T on v_mfma_f32_16x16x32_bf16: keys are the M side,
 //      the head group (zero-padded to 16) is N, d = 256 is the contraction.
 //      Q lives in registers for the whole item;
@@ -44,8 +45,12 @@
 //      into the fp32 accumulator;
 //   6. epilogue: O / l rounded to bf16 (RNE), lse = ln 2 * (m + log2 l); an
 //      empty row writes +0.0 and -inf.
-// The loads of tile j+1 are issued right after tile j has been written to
-// LDS and are in flight while tile j is computed; indices run two tiles ahead.
+// Software pipeline: iteration j stores K of tile j and V of tile j-1 to LDS
+// (one store and one new load per pair of rows, so the loads of K of tile
+// j+1 and V of tile j go out spread over the stores rather than as a burst
+// that would fill the texture unit's queues), then issues the score MFMAs of
+// tile j and finishes tile j-1; the two are independent, so the MFMAs run
+// under the softmax. Indices run three tiles ahead of the scores.
 //
 // Split lists (decode). With one query per request there are too few items
 // to fill the chip, so each item's list can be cut into n_splits ranges of
@@ -159,26 +164,44 @@ __device__ __forceinline__ int32_t load_tile_idx(__amdgpu_buffer_rsrc_t ri, int 
     return __builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)((j * kNK + (lane & 15)) >> blk_shift) * 4u, 0, 0);
 }
 
-// K and V of one tile, row-contiguous. Instruction i covers rows 2i and
-// 2i+1: lane l reads 16-byte chunk l & 31 of row 2i + (l >> 5). `off` holds,
-// in lane r < 16, the byte offset of key row r (kOob when masked).
-__device__ __forceinline__ void load_tile_kv(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                             uint32_t off, u32x4_t (&ks)[8], u32x4_t (&vs)[8],
-                                             int lane) {
-    const bool upper = (lane >> 5) != 0;
-    const uint32_t ch = (uint32_t)(lane & 31) << 4;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t o0 = __builtin_amdgcn_readlane(off, 2 * i);
-        const uint32_t o1 = __builtin_amdgcn_readlane(off, 2 * i + 1);
-        const uint32_t o = (upper ? o1 : o0) + ch;
-        ks[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
-        vs[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0);
-    }
+// DPP row_newbcast:N (gfx90a and later): lane N of each 16-lane row is
+// broadcast to the whole row.
+template <int N>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + N, 0xF, 0xF, false);
 }
 
-__device__ __forceinline__ void store_tile_kv(uint8_t *lk, uint8_t *lv, const u32x4_t (&ks)[8],
-                                              const u32x4_t (&vs)[8], int lane) {
+// Byte offsets of the 8 row-pair loads of one tile. Load i covers rows 2i and
+// 2i+1: lane l reads 16-byte chunk l & 31 of row 2i + (l >> 5). `off` holds,
+// in every lane l, the byte offset of key row l & 15 (kOob when masked).
+// Rows 2 and 3 of the wave (lanes 32..63) first take their right neighbour's
+// offset (row_shl:1), so one row broadcast of lane 2i gives row 2i to lanes
+// 0..31 and row 2i+1 to lanes 32..63; the chunk offset is added in the same
+// DPP instruction.
+struct TileOffsets {
+    uint32_t o[8];
+};
+__device__ __forceinline__ TileOffsets tile_offsets(uint32_t off, int lane) {
+    const uint32_t ch = (uint32_t)(lane & 31) << 4;
+    const uint32_t off2 = (uint32_t)__builtin_amdgcn_update_dpp((int)off, (int)off, 0x101, 0xC, 0xF, false);
+    TileOffsets t;
+    t.o[0] = row_bcast<0>(off2) + ch;
+    t.o[1] = row_bcast<2>(off2) + ch;
+    t.o[2] = row_bcast<4>(off2) + ch;
+    t.o[3] = row_bcast<6>(off2) + ch;
+    t.o[4] = row_bcast<8>(off2) + ch;
+    t.o[5] = row_bcast<10>(off2) + ch;
+    t.o[6] = row_bcast<12>(off2) + ch;
+    t.o[7] = row_bcast<14>(off2) + ch;
+    return t;
+}
+// K of tile j goes to LDS while K of tile j+1 is requested; V of tile j-1
+// goes to LDS while V of tile j is requested (a store and a load per pair of
+// rows, so the loads are spread out).
+__device__ __forceinline__ void rotate_tiles(uint8_t *lk, uint8_t *lv, __amdgpu_buffer_rsrc_t rk,
+                                             __amdgpu_buffer_rsrc_t rv, const TileOffsets &tk,
+                                             const TileOffsets &tv, u32x4_t (&ks)[8], u32x4_t (&vs)[8],
+                                             int lane) {
     const int half = lane >> 5;
     const int c = lane & 31;
     uint8_t *kb = lk + half * kKStride + c * 16;
@@ -186,7 +209,9 @@ __device__ __forceinline__ void store_tile_kv(uint8_t *lk, uint8_t *lv, const u3
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         *(u32x4_t *)(kb + 2 * i * kKStride) = ks[i];
+        ks[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, tk.o[i], 0, 0);
         *(u32x4_t *)(vb + 2 * i * kVStride) = vs[i];
+        vs[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, tv.o[i], 0, 0);
     }
 }
 
@@ -383,28 +408,41 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
                 return sl.mask;
         };
 
-        // Tile j+1 is loaded into registers while tile j, already in LDS, is
-        // computed; the indices of tile j+2 are loaded alongside. Loads are
-        // issued even past the last tile (all slots masked there: nothing is
-        // fetched), so every iteration runs the same memory instructions.
+        // Software pipeline, one tile deep: iteration j writes K of tile j
+        // and V of tile j-1 to LDS, requests K of tile j+1 and V of tile j,
+        // then computes the scores of tile j and finishes tile j-1 (softmax,
+        // weighted values). The two halves are independent, so the MFMAs of
+        // one overlap the vector work of the other. Loads past the range are
+        // masked (nothing fetched); the loop runs one iteration past the last
+        // tile to finish it.
         u32x4_t ks[8], vs[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vs[i] = (u32x4_t){0u, 0u, 0u, 0u};
         Slot cur, nxt;
         int32_t i0 = load_tile_idx(ri, j_begin, shift, lane);
         int32_t inext = load_tile_idx(ri, j_begin + 1, shift, lane);
-        load_tile_kv(rk, rv, prep(j_begin, i0, cur), ks, vs, lane);
+        uint32_t off_cur = prep(j_begin, i0, cur);
+        {
+            const TileOffsets t0 = tile_offsets(off_cur, lane);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ks[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, t0.o[i], 0, 0);
+        }
         int32_t inext2 = load_tile_idx(ri, j_begin + 2, shift, lane);
+        f32x4_t s_prev = {0.f, 0.f, 0.f, 0.f};
+        uint32_t mask_prev = 0;
         for (int j = j_begin;; ++j) {
-            store_tile_kv(lk, lv, ks, vs, lane);
-            load_tile_kv(rk, rv, prep(j + 1, inext, nxt), ks, vs, lane);
+            const uint32_t off_next = prep(j + 1, inext, nxt);
+            rotate_tiles(lk, lv, rk, rv, tile_offsets(off_next, lane), tile_offsets(off_cur, lane), ks, vs, lane);
             inext = inext2;
             inext2 = load_tile_idx(ri, j + 3, shift, lane);
             const uint32_t mask = tile_mask(cur);
-            if (mask) {
-                const f32x4_t sc = tile_scores(lk, qb, lane);
-                tile_finish(sc, lv, mask, o, st, p.scale_log2, lane);
-            }
-            if (j + 1 >= j_end) break;
+            const f32x4_t sc = tile_scores(lk, qb, lane);
+            if (mask_prev) tile_finish(s_prev, lv, mask_prev, o, st, p.scale_log2, lane);
+            if (j >= j_end) break;
+            s_prev = sc;
+            mask_prev = mask;
             cur = nxt;
+            off_cur = off_next;
         }
     }
 
