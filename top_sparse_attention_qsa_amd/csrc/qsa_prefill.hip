@@ -181,7 +181,23 @@ __device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
 struct TileOffsets {
     uint32_t o[8];
 };
+template <bool kReadlane>
 __device__ __forceinline__ TileOffsets tile_offsets(uint32_t off, int lane) {
+    if constexpr (kReadlane) {
+        // the same offsets through scalar registers: slower to form, but the
+        // loads that use them then go out paced by that work, which the
+        // micro-block gather (runs of 4 neighbouring rows) prefers
+        const bool upper = (lane >> 5) != 0;
+        const uint32_t ch = (uint32_t)(lane & 31) << 4;
+        TileOffsets t;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t o0 = __builtin_amdgcn_readlane(off, 2 * i);
+            const uint32_t o1 = __builtin_amdgcn_readlane(off, 2 * i + 1);
+            t.o[i] = (upper ? o1 : o0) + ch;
+        }
+        return t;
+    }
     const uint32_t ch = (uint32_t)(lane & 31) << 4;
     const uint32_t off2 = (uint32_t)__builtin_amdgcn_update_dpp((int)off, (int)off, 0x101, 0xC, 0xF, false);
     TileOffsets t;
@@ -250,18 +266,20 @@ __device__ __forceinline__ void tile_finish(f32x4_t s, const uint8_t *lv, uint32
     const int jg = lane >> 4;
 
     float x[4];
-    float tmax = -INFINITY;
+    float lmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         x[r] = ((mask >> (jg * 4 + r)) & 1u) ? s[r] * scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, x[r]);
+        lmax = fmaxf(lmax, x[r]);
     }
-    // The tile has at least one valid key (the caller skips empty tiles), so
-    // tmax is finite for every head. The reference max only moves when a
-    // head's tile max exceeds it by more than kRescaleSlack (base-2 units):
-    // weights stay below 2^kRescaleSlack and the O/l rescale is rare.
-    tmax = wave_max_across_groups(tmax);
-    if (__ballot(tmax > st.m + kRescaleSlack)) {
+    // The reference max only moves when some key's logit exceeds it by more
+    // than kRescaleSlack (base-2 units): weights stay below 2^kRescaleSlack
+    // and the O/l rescale is rare. The test needs only this lane's 4 keys and
+    // a ballot; the head's max over its 16 keys (four lanes) is taken only
+    // when the rescale happens. The tile has at least one valid key (the
+    // caller skips empty tiles), so that max is finite for every head.
+    if (__ballot(lmax > st.m + kRescaleSlack)) {
+        const float tmax = wave_max_across_groups(lmax);
         const float m_new = fmaxf(st.m, tmax);
         const float alpha = __builtin_amdgcn_exp2f(st.m - m_new); // 0 on the first tile
         st.l *= alpha;
@@ -333,6 +351,9 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int32_t row = rest % p.T;
     const int32_t g = rest / p.T;
     constexpr bool kIsPool = kMode == kPool;
+    // measured per index form: micro-block lists run 8% faster with the row
+    // offsets formed through readlane, token lists 1% faster with DPP
+    constexpr bool kRlOffsets = kMode == kBlocks;
     // absolute position of this query
     const int64_t tq = kIsPool ? (int64_t)p.q_pos[row] : p.q_pos0 + row;
     const int h0 = g * p.G + hc * 16;
@@ -423,7 +444,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
         int32_t inext = load_tile_idx(ri, j_begin + 1, shift, lane);
         uint32_t off_cur = prep(j_begin, i0, cur);
         {
-            const TileOffsets t0 = tile_offsets(off_cur, lane);
+            const TileOffsets t0 = tile_offsets<kRlOffsets>(off_cur, lane);
 #pragma unroll
             for (int i = 0; i < 8; ++i) ks[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, t0.o[i], 0, 0);
         }
@@ -432,7 +453,8 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
         uint32_t mask_prev = 0;
         for (int j = j_begin;; ++j) {
             const uint32_t off_next = prep(j + 1, inext, nxt);
-            rotate_tiles(lk, lv, rk, rv, tile_offsets(off_next, lane), tile_offsets(off_cur, lane), ks, vs, lane);
+            rotate_tiles(lk, lv, rk, rv, tile_offsets<kRlOffsets>(off_next, lane),
+                         tile_offsets<kRlOffsets>(off_cur, lane), ks, vs, lane);
             inext = inext2;
             inext2 = load_tile_idx(ri, j + 3, shift, lane);
             const uint32_t mask = tile_mask(cur);
