@@ -380,3 +380,104 @@ def test_decode_workspace_reuse_and_checks():
     assert a[0].shape[0] == 4
     with pytest.raises(qsa.QsaError):
         run_decode(*args, workspace=ws[: need - 16])
+
+
+# ------------------------------------------------------------------ largest caches
+
+
+QSA_MAX_KV_ROWS = 4194303  # include/qsa.h: T_kv * Hkv * 512 bytes must stay below 2^31
+
+
+def _reference_rows(q, k_rows, v_rows, lists, positions, scale):
+    """Oracle outputs from the oracle's own per-row steps, with K/V given only
+    for the rows that may be read (dicts position -> bf16 bits [Hkv, 256])."""
+    T, Hq = q.shape[0], q.shape[1]
+    Hkv = lists.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((T, Hq, 256))
+    lse = np.full((T, Hq), -np.inf)
+    for i in range(T):
+        q_t = oracle.bf16_to_f64(q[i])
+        for g in range(Hkv):
+            sel = positions(lists[i, g], i)
+            k_sel = np.stack([oracle.bf16_to_f64(k_rows[s][g]) for s in sel]) if sel else np.zeros((0, 256))
+            v_sel = np.stack([oracle.bf16_to_f64(v_rows[s][g]) for s in sel]) if sel else np.zeros((0, 256))
+            for h in range(g * G, (g + 1) * G):
+                o, l, _ = oracle.attend(q_t[h], k_sel, v_sel, scale)
+                out[i, h], lse[i, h] = o, l
+    return out, lse
+
+
+def _device_kv(n_rows, Hkv, seed):
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    k = torch.randn((n_rows, Hkv, 256), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((n_rows, Hkv, 256), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    return k, v
+
+
+def _rows_to_host(t, rows):
+    rows = sorted(set(int(r) for r in rows))
+    idx = torch.tensor(rows, dtype=torch.int64, device="cuda")
+    got = torch_bf16_to_numpy_bits(t.index_select(0, idx))
+    return {r: got[i] for i, r in enumerate(rows)}
+
+
+@pytest.mark.parametrize("Hkv", [1, 2])
+def test_extend_at_the_largest_cache(Hkv):
+    """T_kv * Hkv = QSA_MAX_KV_ROWS: the last K/V rows sit just below 2^31
+    bytes; the lists name them, rows near 2^21 and 2^22, and random ones."""
+    T_kv = QSA_MAX_KV_ROWS // Hkv
+    T, Hq, K = 48, 6 * Hkv, 320
+    p0 = T_kv - T
+    progress(f"largest cache: T_kv={T_kv}, Hkv={Hkv} ({2 * T_kv * Hkv * 512 / 2**30:.2f} GiB of K/V)")
+    k, v = _device_kv(T_kv, Hkv, seed=900 + Hkv)
+    rng = np.random.default_rng(901 + Hkv)
+    q = rand_bf16(rng, (T, Hq, 256))
+    idx = np.full((T, Hkv, K), -1, np.int32)
+    for t in range(T):
+        pos = p0 + t
+        for g in range(Hkv):
+            fixed = [pos, pos - 1, T_kv - 1, T_kv - T - 1, (1 << 22) - 1, 1 << 21, 0, T_kv, T_kv + 5]
+            rand = list(rng.integers(0, pos + 1, size=K - len(fixed) - 20))
+            row = np.array(fixed + rand + [-1] * 20, np.int64)
+            rng.shuffle(row)
+            idx[t, g] = row
+    out, lse = host(*qsa.sparse_prefill_extend(dev_bf16(q), k, v, dev_i32(idx), p0))
+    used = idx[(idx >= 0) & (idx < T_kv)]
+    k_rows, v_rows = _rows_to_host(k, used), _rows_to_host(v, used)
+    del k, v
+    torch.cuda.empty_cache()
+    ref_out, ref_lse = _reference_rows(q, k_rows, v_rows, idx,
+                                       lambda lst, i: oracle.selected_positions(lst, p0 + i), 1 / 16)
+    progress(f"largest cache Hkv={Hkv}: {compare(out, lse, ref_out, ref_lse, label='largest cache')}")
+
+
+def test_pool_and_decode_at_the_largest_pool():
+    """A pool of QSA_MAX_KV_ROWS slots (one KV head): rows in the last slots,
+    positions permuted over the whole pool."""
+    n_slots, Hq, K = QSA_MAX_KV_ROWS, 8, 260
+    k, v = _device_kv(n_slots, 1, seed=910)
+    rng = np.random.default_rng(911)
+    slot_pos = np.full(n_slots, -1, np.int32)
+    live = rng.choice(n_slots, size=100000, replace=False)
+    live[:4] = [n_slots - 1, n_slots - 2, n_slots - 3, 0]
+    slot_pos[live] = rng.integers(0, 50000, size=live.size)
+    T = 24
+    q = rand_bf16(rng, (T, Hq, 256))
+    q_pos = rng.integers(20000, 50000, size=T).astype(np.int32)
+    idx = np.full((T, 1, K), -1, np.int32)
+    for t in range(T):
+        row = list(live[:4]) + list(rng.choice(live, size=K - 14)) + [n_slots, -3] + [-1] * 8
+        idx[t, 0] = np.array(row[:K], np.int64)
+    args = (dev_bf16(q), k, v, dev_i32(idx), dev_i32(q_pos), dev_i32(slot_pos))
+    out, lse = host(*qsa.sparse_prefill_pool(*args))
+    dout, dlse = host(*qsa.sparse_decode(*args))
+    used = idx[(idx >= 0) & (idx < n_slots)]
+    k_rows, v_rows = _rows_to_host(k, used), _rows_to_host(v, used)
+    del k, v, args
+    torch.cuda.empty_cache()
+    ref_out, ref_lse = _reference_rows(q, k_rows, v_rows, idx,
+                                       lambda lst, i: oracle.pool_selected_slots(lst, int(q_pos[i]), slot_pos),
+                                       1 / 16)
+    compare(out, lse, ref_out, ref_lse, label="largest pool")
+    compare(dout, dlse, ref_out, ref_lse, label="largest pool, decode")

@@ -32,11 +32,12 @@
 //      the head group (zero-padded to 16) is N, d = 256 is the contraction.
 //      Q lives in registers for the whole item;
 //   4. online softmax in fp32, base 2. In the S^T layout a lane holds 4 keys
-//      of one head: the row max is an in-lane max plus two lane-swap steps
-//      (v_permlane16_swap / v_permlane32_swap); the row sums stay per lane
-//      until the epilogue. The reference max only
-//      moves when a tile max exceeds it by a slack of 2^8, so rescaling the
-//      accumulators is rare;
+//      of one head. The reference max only moves when some logit exceeds it
+//      by a slack of 2^8, so rescaling the accumulators is rare: each lane
+//      tests its 4 keys and a ballot decides; only then is the head's max
+//      over its 16 keys taken (in-lane max plus two lane-swap steps,
+//      v_permlane16_swap / v_permlane32_swap). The row sums stay per lane
+//      until the epilogue;
 //   5. O^T += V_tile^T . P^T on v_mfma_f32_16x16x32_bf16: V^T comes out of
 //      LDS with ds_read_b64_tr_b16 (a 4x16 bf16 block transposed across 16
 //      lanes); P^T is already in the B-operand layout. Each weight is sent as
@@ -76,7 +77,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
