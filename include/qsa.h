@@ -162,9 +162,10 @@ qsa_status_t qsa_sparse_prefill_blocks(const void *q, const void *k, const void 
  *
  * Errors: QSA_ERR_INVALID_ARG for total_q < 0, n_slots < 0, either above
  * INT32_MAX, Hq < 1, Hkv < 1, K < 0, Hq % Hkv != 0, a non-finite scale, a
- * null pointer that would be used (q_pos and slot_pos are used whenever
- * total_q > 0) or out/lse equal to an input pointer; QSA_ERR_UNSUPPORTED when
- * n_slots * Hkv > QSA_MAX_KV_ROWS or K > 2^28.
+ * null pointer that would be used (q_pos is used whenever total_q > 0;
+ * slot_pos, k_pool and v_pool may be NULL when n_slots == 0, every slot then
+ * being masked) or out/lse equal to an input pointer;
+ * QSA_ERR_UNSUPPORTED when n_slots * Hkv > QSA_MAX_KV_ROWS or K > 2^28.
  */
 qsa_status_t qsa_sparse_prefill_pool(const void *q, const void *k_pool, const void *v_pool,
                                      const int32_t *slot_idx, const int32_t *q_pos,

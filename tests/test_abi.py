@@ -129,6 +129,7 @@ def call_pool(lib, total_q=8, n_slots=40, Hq=4, Hkv=2, K=5, scale=0.0625, q_pos=
     (dict(out=QP), INVALID), (dict(lse=SP), INVALID), (dict(scale=float("inf")), INVALID),
     (dict(n_slots=4194304, Hkv=1, Hq=1), UNSUPPORTED), (dict(K=(1 << 28) + 1), UNSUPPORTED),
     (dict(total_q=0), OK), (dict(total_q=0, q_pos=None, slot_pos=None), OK),
+    (dict(n_slots=0, q_pos=None), INVALID), (dict(n_slots=0, idx=None), INVALID),
 ])
 def test_pool_argument_rules(lib, kwargs, expect):
     assert call_pool(lib, **kwargs) == expect

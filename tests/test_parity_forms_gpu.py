@@ -282,6 +282,12 @@ def test_pool_edge_cases():
     # zero selection width
     out, lse = run_pool(q, k, v, np.zeros((6, 2, 0), np.int32), q_pos, slot_pos)
     assert np.all(out == 0) and np.all(np.isneginf(lse))
+    # an empty pool: every listed slot is outside it
+    empty = np.zeros((0, 2, 256), np.uint16)
+    out, lse = run_pool(q, empty, empty, idx, q_pos, np.zeros(0, np.int32))
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+    out, lse = run_decode(q, empty, empty, idx, q_pos, np.zeros(0, np.int32))
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
 
 
 def test_pool_binding_validates():

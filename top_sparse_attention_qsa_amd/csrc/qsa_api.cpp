@@ -32,7 +32,9 @@ qsa_status_t check_common(const void *q, const void *k, const void *v, const int
     if (!isfinite(scale)) return QSA_ERR_INVALID_ARG;
     if (T == 0) return QSA_OK;
     if (q == nullptr || out == nullptr || lse == nullptr) return QSA_ERR_INVALID_ARG;
-    if (n_entries > 0 && (k == nullptr || v == nullptr || idx == nullptr)) return QSA_ERR_INVALID_ARG;
+    if (n_entries > 0 && idx == nullptr) return QSA_ERR_INVALID_ARG;
+    // K/V rows are read only when there are some (a pool may be empty)
+    if (n_entries > 0 && n_kv_rows > 0 && (k == nullptr || v == nullptr)) return QSA_ERR_INVALID_ARG;
     if (aliases(out, lse, {q, k, v, (const void *)idx})) return QSA_ERR_INVALID_ARG;
     if (n_kv_rows * (int64_t)Hkv > QSA_MAX_KV_ROWS) return QSA_ERR_UNSUPPORTED;
     if (((int64_t)n_entries << blk_shift) > kMaxK) return QSA_ERR_UNSUPPORTED;
@@ -52,6 +54,7 @@ qsa::PrefillArgs make_args(const void *q, const void *k, const void *v, const in
     a.k = k;
     a.v = v;
     a.idx = idx;
+    a.pool = false;
     a.q_pos = nullptr;
     a.slot_pos = nullptr;
     a.out = out;
@@ -146,10 +149,11 @@ qsa_status_t qsa_sparse_prefill_pool(const void *q, const void *k_pool, const vo
     const qsa_status_t st =
         check_common(q, k_pool, v_pool, slot_idx, total_q, n_slots, Hq, Hkv, K, 0, scale, out, lse);
     if (st != QSA_OK || total_q == 0) return st;
-    if (q_pos == nullptr || slot_pos == nullptr) return QSA_ERR_INVALID_ARG;
+    if (q_pos == nullptr || (slot_pos == nullptr && n_slots > 0)) return QSA_ERR_INVALID_ARG;
     if (aliases(out, lse, {(const void *)q_pos, (const void *)slot_pos})) return QSA_ERR_INVALID_ARG;
     qsa::PrefillArgs a =
         make_args(q, k_pool, v_pool, slot_idx, total_q, n_slots, 0, Hq, Hkv, K, 0, scale, out, lse);
+    a.pool = true;
     a.q_pos = q_pos;
     a.slot_pos = slot_pos;
     return run(a, stream);
@@ -167,7 +171,8 @@ qsa_status_t qsa_sparse_decode(const void *q, const void *k_pool, const void *v_
     const qsa_status_t st =
         check_common(q, k_pool, v_pool, slot_idx, n_req, n_slots, Hq, Hkv, K, 0, scale, out, lse);
     if (st != QSA_OK || n_req == 0) return st;
-    if (q_pos == nullptr || slot_pos == nullptr || workspace_bytes < 0) return QSA_ERR_INVALID_ARG;
+    if (q_pos == nullptr || (slot_pos == nullptr && n_slots > 0) || workspace_bytes < 0)
+        return QSA_ERR_INVALID_ARG;
     if (aliases(out, lse, {(const void *)q_pos, (const void *)slot_pos, workspace})) return QSA_ERR_INVALID_ARG;
     const qsa::SplitPlan plan = qsa::plan_split(n_req, Hq, Hkv, K);
     const int64_t need = qsa::split_workspace_bytes(n_req, Hq, plan);
@@ -179,6 +184,7 @@ qsa_status_t qsa_sparse_decode(const void *q, const void *k_pool, const void *v_
             if (in == workspace) return QSA_ERR_INVALID_ARG;
     }
     qsa::PrefillArgs a = make_args(q, k_pool, v_pool, slot_idx, n_req, n_slots, 0, Hq, Hkv, K, 0, scale, out, lse);
+    a.pool = true;
     a.q_pos = q_pos;
     a.slot_pos = slot_pos;
     a.n_splits = plan.n_splits;

@@ -15,8 +15,10 @@ struct PrefillArgs {
     const void *k;           // bf16 [n_kv_rows, Hkv, 256]
     const void *v;           // bf16 [n_kv_rows, Hkv, 256]
     const int32_t *idx;      // int32 [T, Hkv, K]
-    const int32_t *q_pos;    // pool mode: int32 [T] query positions, else null
-    const int32_t *slot_pos; // pool mode: int32 [n_kv_rows] slot positions, else null
+    bool pool;               // entries are pool slots (q_pos, slot_pos used)
+    const int32_t *q_pos;    // pool form: int32 [T] query positions
+    const int32_t *slot_pos; // pool form: int32 [n_kv_rows] slot positions (may be
+                             // null when n_kv_rows == 0)
     void *out;               // bf16 [T, Hq, 256]
     float *lse;              // fp32 [T, Hq]
     int64_t T;               // query rows

@@ -618,7 +618,7 @@ qsa_status_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     if (a.n_splits > 1) {
         // pool form only (decode); workspace: [pairs * n_splits] (m, l, le, 0)
         // records, then [pairs * n_splits * 256] fp32 partial O
-        if (!a.slot_pos || a.workspace == nullptr) return QSA_ERR_INVALID_ARG;
+        if (!a.pool || a.workspace == nullptr) return QSA_ERR_INVALID_ARG;
         const int64_t split_items = n_items * a.n_splits;
         if (split_items > INT32_MAX - 4) return QSA_ERR_UNSUPPORTED;
         kp.n_items = (int32_t)split_items;
@@ -628,7 +628,7 @@ qsa_status_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
         kp.ws_o = (float *)((f32x4_t *)a.workspace + a.T * a.Hq * a.n_splits);
         return launch<4, kPool, true>(kp, stream);
     }
-    if (a.slot_pos) return launch<4, kPool, false>(kp, stream);
+    if (a.pool) return launch<4, kPool, false>(kp, stream);
     return a.blk_shift ? launch<4, kBlocks, false>(kp, stream) : launch<4, kTokens, false>(kp, stream);
 }
 
