@@ -487,3 +487,44 @@ def test_pool_and_decode_at_the_largest_pool():
                                        1 / 16)
     compare(out, lse, ref_out, ref_lse, label="largest pool")
     compare(dout, dlse, ref_out, ref_lse, label="largest pool, decode")
+
+
+@pytest.mark.parametrize("hq,hkv", [(40, 2), (17, 1), (32, 1)])
+def test_decode_and_blocks_with_several_head_chunks(hq, hkv):
+    """More than 16 query heads per KV head: each list is computed by several
+    waves (16 heads each), and in decode each of those by several ranges."""
+    rng = np.random.default_rng(hq * 10 + hkv)
+    n_slots, K, n_req = 2000, 700, 5
+    k, v = rand_bf16(rng, (n_slots, hkv, 256)), rand_bf16(rng, (n_slots, hkv, 256))
+    slot_pos = rng.permutation(n_slots).astype(np.int32)
+    q = rand_bf16(rng, (n_req, hq, 256))
+    q_pos = rng.integers(500, n_slots, size=n_req).astype(np.int32)
+    idx = rng.integers(-3, n_slots + 3, size=(n_req, hkv, K)).astype(np.int32)
+    assert qsa.decode_workspace_bytes(n_req, hq, hkv, K) > 0
+    out, lse = run_decode(q, k, v, idx, q_pos, slot_pos)
+    ref_out, ref_lse = oracle.sparse_prefill_pool(q, k, v, idx, q_pos, slot_pos)
+    compare(out, lse, ref_out, ref_lse, label=f"decode ({hq},{hkv})")
+    # micro-blocks with the same head shape
+    T = 70
+    qb = rand_bf16(rng, (T, hq, 256))
+    kb, vb = rand_bf16(rng, (T, hkv, 256)), rand_bf16(rng, (T, hkv, 256))
+    bidx = rng.integers(-1, T // 4 + 2, size=(T, hkv, 9)).astype(np.int32)
+    out, lse = run_blocks(qb, kb, vb, bidx, 4)
+    ref_out, ref_lse = oracle.sparse_prefill_blocks(qb, kb, vb, bidx, 4)
+    compare(out, lse, ref_out, ref_lse, label=f"blocks ({hq},{hkv})")
+
+
+def test_pool_extreme_positions():
+    """Query positions and slot positions at the int32 extremes."""
+    rng = np.random.default_rng(77)
+    n_slots = 64
+    k, v = rand_bf16(rng, (n_slots, 1, 256)), rand_bf16(rng, (n_slots, 1, 256))
+    slot_pos = rng.integers(0, 1000, size=n_slots).astype(np.int32)
+    slot_pos[:4] = [INT32_MAX, INT32_MIN, INT32_MAX - 1, 0]
+    q = rand_bf16(rng, (5, 3, 256))
+    q_pos = np.array([INT32_MAX, INT32_MAX - 1, INT32_MIN, 0, 999], np.int32)
+    idx = np.tile(np.arange(n_slots, dtype=np.int32), (5, 1, 1))
+    out, lse = run_pool(q, k, v, idx, q_pos, slot_pos)
+    ref_out, ref_lse = oracle.sparse_prefill_pool(q, k, v, idx, q_pos, slot_pos)
+    compare(out, lse, ref_out, ref_lse, label="pool extremes")
+    assert np.all(np.isneginf(lse[2]))
