@@ -19,8 +19,8 @@ algorithmic bytes per launch divided by the mean kernel duration, measured
 with HIP events on the stream the kernel runs on, against MI355X's 8 TB/s.
 `traffic` comes from committed rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs
 of this same command, scaled by the counters' reading on a copy kernel of
-known size, and is reported only while the kernel source still matches the
-one the counters were taken on.
+known size, and is reported only while the built library is byte-identical
+to the one the counters were taken on.
 
 Other workloads (--workload): any of the token workloads c1..c6, the
 micro-block workloads c7/c8 (entries name 4-token blocks, the model's
@@ -39,15 +39,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCES = ("top_sparse_attention_qsa_amd/csrc/qsa_prefill.hip",)
+LIBRARY = "top_sparse_attention_qsa_amd/lib/libqsa.so"
 METRIC = "QSA sparse prefill query-tokens/s and gathered-KV GB/s (% HBM roofline), 1 GPU"
 
 
 def kernel_sha() -> str:
+    """First 16 hex digits of the sha256 of the built library: the code that
+    runs (the build is deterministic, so comment-only edits keep it)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    with open(os.path.join(ROOT, LIBRARY), "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 
