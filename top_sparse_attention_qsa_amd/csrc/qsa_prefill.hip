@@ -499,68 +499,56 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
-// Full-wave reductions for the merge kernel (six butterfly steps of lane
-// shuffles; the merge is small and off the gather's critical path).
-__device__ __forceinline__ float wave_max64(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-__device__ __forceinline__ float wave_sum64(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
-// Merge of the n_splits partials of each (row, head): one wave per pair.
-// The (m, l, le) records are spread over the lanes for the max and the two
-// sums; then lane l accumulates d = 4l .. 4l+3 over the ranges, eight partial
-// rows in flight at a time. A range with no valid key has m = -inf and weight
+// Merge of the n_splits partials of each (row, head): one wave per pair,
+// lane l owning d = 4l .. 4l+3. Up to 16 ranges are taken per round: their
+// (m, l, le) records and partial rows are all requested before any is used,
+// then folded into a running result whose reference max M moves when a
+// round's max exceeds it. A range with no valid key has m = -inf and weight
 // 0; a row with none at all gets +0.0 and lse = -inf.
 template <int WPB>
 __global__ __launch_bounds__(64 * WPB) void qsa_combine_kernel(const float *__restrict__ ws_o,
                                                                const f32x4_t *__restrict__ ws_ml,
                                                                uint16_t *__restrict__ out, float *__restrict__ lse,
                                                                int32_t n_pairs, int32_t n_splits) {
+    constexpr int kRound = 16;
     const int lane = threadIdx.x & 63;
     const int32_t pair = (int32_t)blockIdx.x * WPB + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (pair >= n_pairs) return;
     const f32x4_t *ml = ws_ml + (int64_t)pair * n_splits;
     const float *po = ws_o + (int64_t)pair * n_splits * kD + lane * 4;
 
-    float mloc = -INFINITY;
-    for (int s = lane; s < n_splits; s += 64) mloc = fmaxf(mloc, ml[s][0]);
-    const float M = wave_max64(mloc);
+    float M = -INFINITY, L = 0.f, LE = 0.f;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    float L = 0.f, LE = 0.f;
-    if (M != -INFINITY) {
-        float lloc = 0.f, leloc = 0.f;
-        for (int s = lane; s < n_splits; s += 64) {
-            const f32x4_t m = ml[s];
-            const float w = m[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[0] - M);
-            lloc += w * m[1];
-            leloc += w * m[2];
-        }
-        L = wave_sum64(lloc);
-        LE = wave_sum64(leloc);
-        int s = 0;
-        for (; s + 8 <= n_splits; s += 8) {
-            f32x4_t part[8];
-            float w[8];
+    for (int s0 = 0; s0 < n_splits; s0 += kRound) {
+        const int n = min(kRound, n_splits - s0);
+        f32x4_t rec[kRound], part[kRound];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                part[u] = *(const f32x4_t *)(po + (int64_t)(s + u) * kD);
-                const float m = ml[s + u][0];
-                w[u] = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+        for (int u = 0; u < kRound; ++u) {
+            if (u < n) {
+                rec[u] = ml[s0 + u];
+                part[u] = *(const f32x4_t *)(po + (int64_t)(s0 + u) * kD);
+            } else {
+                rec[u] = (f32x4_t){-INFINITY, 0.f, 0.f, 0.f};
+                part[u] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
             }
+        }
+        float cm = -INFINITY;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) acc += w[u] * part[u];
+        for (int u = 0; u < kRound; ++u) cm = fmaxf(cm, rec[u][0]);
+        const float Mn = fmaxf(M, cm);
+        if (Mn == -INFINITY) continue;
+        const float a = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        acc *= a;
+        L *= a;
+        LE *= a;
+#pragma unroll
+        for (int u = 0; u < kRound; ++u) {
+            const float w = rec[u][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rec[u][0] - Mn);
+            acc += w * part[u];
+            L += w * rec[u][1];
+            LE += w * rec[u][2];
         }
-        for (; s < n_splits; ++s) {
-            const float m = ml[s][0];
-            const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-            acc += w * *(const f32x4_t *)(po + (int64_t)s * kD);
-        }
+        M = Mn;
     }
     const bool empty = !(L > 0.f);
     const float inv = empty ? 0.f : 1.0f / L;
