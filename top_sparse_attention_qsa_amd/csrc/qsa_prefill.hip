@@ -11,9 +11,9 @@
 // selected slots of (t, g). Items are independent, so waves never synchronise
 // with each other; a block is WPB such waves. Items are numbered KV-head
 // major, and blocks are renumbered so that each XCD (block b runs on XCD
-// b % 8) works through one contiguous range of items: the waves sharing an
-// XCD's L2 hold neighbouring query positions of one KV head, whose local
-// windows, sinks and nearby picks overlap.
+// b % 8) takes runs of consecutive items: the waves sharing an XCD's L2 hold
+// neighbouring query positions of one KV head, whose local windows, sinks
+// and nearby picks overlap.
 //
 // Per wave, the K list is walked in tiles of 16 slots:
 //   1. one buffer load brings the tile's indices, lane l holding slot l & 15;
@@ -116,12 +116,19 @@ struct KParams {
 };
 
 // Blocks are dealt round-robin over the 8 XCDs (block b runs on XCD b % 8).
-// Renumber so each XCD works on one contiguous range of items: neighbouring
-// query positions share their local window and sink rows in that XCD's L2.
-__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t nb) {
-    const uint32_t q = nb >> 3, r = nb & 7u;
-    const uint32_t x = b & 7u, i = b >> 3;
-    return x * q + (x < r ? x : r) + i;
+// Renumber in groups of 8 * kXcdChunk blocks: within a group, XCD x takes
+// kXcdChunk consecutive item blocks (256 query rows at 4 items per block), so
+// neighbouring query positions share their window and sink rows in that XCD's
+// L2, while all XCDs move through the rows together and draw on the same part
+// of the cache at the same time. (One contiguous range per XCD was 7-8% slower
+// on the (24,2) and 235K-token workloads; plain round-robin is 20% slower on
+// the former.) Blocks past the last whole group keep their number.
+constexpr uint32_t kXcdChunk = 64;
+__device__ __forceinline__ uint32_t xcd_chunked(uint32_t b, uint32_t nb) {
+    const uint32_t full = nb / (8 * kXcdChunk) * (8 * kXcdChunk);
+    if (b >= full) return b;
+    const uint32_t g = b / (8 * kXcdChunk), bl = b % (8 * kXcdChunk);
+    return g * 8 * kXcdChunk + (bl & 7u) * kXcdChunk + (bl >> 3);
 }
 
 // Reductions over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows
@@ -342,7 +349,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int32_t item = (int32_t)xcd_contiguous(blockIdx.x, gridDim.x) * WPB + w;
+    const int32_t item = (int32_t)xcd_chunked(blockIdx.x, gridDim.x) * WPB + w;
     if (item >= p.n_items) return;
 
     const int32_t sp = kSplit ? item % p.n_splits : 0;
