@@ -528,3 +528,50 @@ def test_pool_extreme_positions():
     ref_out, ref_lse = oracle.sparse_prefill_pool(q, k, v, idx, q_pos, slot_pos)
     compare(out, lse, ref_out, ref_lse, label="pool extremes")
     assert np.all(np.isneginf(lse[2]))
+
+
+# ------------------------------------------------------------------ graph capture
+
+
+def test_calls_replay_from_a_captured_graph():
+    """The entry points allocate nothing and never synchronise, so they can be
+    captured in a HIP graph. Every replay (with eager work and a sync between
+    replays) must equal the eager results bit for bit."""
+    rng = np.random.default_rng(55)
+    T, n_slots = 200, 600
+    q = dev_bf16(rand_bf16(rng, (T, 6, 256)))
+    k, v = dev_bf16(rand_bf16(rng, (T, 2, 256))), dev_bf16(rand_bf16(rng, (T, 2, 256)))
+    idx = dev_i32(rng.integers(-2, T + 2, size=(T, 2, 70)))
+    kp, vp = dev_bf16(rand_bf16(rng, (n_slots, 2, 256))), dev_bf16(rand_bf16(rng, (n_slots, 2, 256)))
+    slot_pos = dev_i32(rng.permutation(n_slots))
+    qd = dev_bf16(rand_bf16(rng, (3, 6, 256)))
+    q_pos = dev_i32(np.array([500, 20, 599]))
+    sidx = dev_i32(rng.integers(-2, n_slots + 2, size=(3, 2, 300)))
+    ws = torch.empty(max(qsa.decode_workspace_bytes(3, 6, 2, 300), 16), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((T, 6, 256), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((T, 6), dtype=torch.float32, device="cuda"),
+            torch.empty((3, 6, 256), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((3, 6), dtype=torch.float32, device="cuda")]
+
+    def calls():
+        qsa.sparse_prefill(q, k, v, idx, out=outs[0], lse=outs[1])
+        qsa.sparse_decode(qd, kp, vp, sidx, q_pos, slot_pos, out=outs[2], lse=outs[3], workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(7.0)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"replay {rep} differs from the eager result"
