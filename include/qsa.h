@@ -36,7 +36,8 @@
  * Ownership and execution: the caller owns every buffer. The library keeps no
  * allocation and no per-call state; it enqueues its kernels on `stream` (a
  * hipStream_t, NULL for the null stream) and returns without synchronising.
- * Inputs are only read; out and lse must not overlap any input or each other.
+ * The device that holds the buffers must be the current HIP device, and
+ * `stream` must belong to it. Inputs are only read; out and lse must not overlap any input or each other.
  * Calls on different streams may run concurrently.
  *
  * Errors: arguments are validated on the host before any HIP call; on error

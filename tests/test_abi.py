@@ -93,6 +93,9 @@ def test_null_index_rejected_only_when_used(lib):
     (dict(p0=-1), INVALID), (dict(T=8, T_kv=11, p0=4), INVALID), (dict(T_kv=-2), INVALID),
     (dict(T=0, T_kv=0, p0=0), OK), (dict(T=0, T_kv=100, p0=100), OK),
     (dict(T=8, T_kv=4194304, p0=0, Hkv=1, Hq=1), UNSUPPORTED),
+    # query positions past the cache, also where q_pos0 + T would overflow int64
+    (dict(T=5, T_kv=10, p0=2 ** 63 - 2), INVALID), (dict(T=2 ** 62, T_kv=2 ** 62, p0=2 ** 62), INVALID),
+    (dict(T=1, T_kv=2 ** 62, p0=2 ** 62), INVALID),
 ])
 def test_extend_argument_rules(lib, kwargs, expect):
     assert call_ext(lib, **kwargs) == expect

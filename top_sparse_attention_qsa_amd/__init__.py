@@ -91,6 +91,14 @@ def _check(status: int, lib) -> None:
         raise QsaError(status, lib.qsa_status_string(status).decode())
 
 
+def _on_device(dev):
+    """Make `dev` the current HIP device for the call (the library launches on
+    the given stream with whatever device is current)."""
+    import torch
+
+    return torch.cuda.device(dev)
+
+
 def _prepare(q, k, v, idx, scale, out, lse):
     import torch
 
@@ -145,8 +153,9 @@ def sparse_prefill(q, k, v, idx, scale=None, out=None, lse=None):
     if k.shape[0] != q.shape[0]:
         raise ValueError("k and v must have T rows; use sparse_prefill_extend for a longer cache")
     T, Hq, Hkv, K = q.shape[0], q.shape[1], k.shape[1], idx.shape[2]
-    st = lib.qsa_sparse_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), T, Hq, Hkv, K,
-                                scale, out.data_ptr(), lse.data_ptr(), stream)
+    with _on_device(q.device):
+        st = lib.qsa_sparse_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), T, Hq, Hkv, K,
+                                    scale, out.data_ptr(), lse.data_ptr(), stream)
     _check(st, lib)
     return out, lse
 
@@ -158,9 +167,10 @@ def sparse_prefill_extend(q, k, v, idx, q_pos0: int, scale=None, out=None, lse=N
     lib = load_library()
     q, k, v, idx, scale, out, lse, stream = _prepare(q, k, v, idx, scale, out, lse)
     T, Hq, Hkv, K = q.shape[0], q.shape[1], k.shape[1], idx.shape[2]
-    st = lib.qsa_sparse_prefill_extend(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), T,
-                                       k.shape[0], int(q_pos0), Hq, Hkv, K, scale, out.data_ptr(),
-                                       lse.data_ptr(), stream)
+    with _on_device(q.device):
+        st = lib.qsa_sparse_prefill_extend(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), T,
+                                           k.shape[0], int(q_pos0), Hq, Hkv, K, scale, out.data_ptr(),
+                                           lse.data_ptr(), stream)
     _check(st, lib)
     return out, lse
 
@@ -174,9 +184,10 @@ def sparse_prefill_blocks(q, k, v, block_idx, q_pos0: int, block_size: int, scal
     lib = load_library()
     q, k, v, block_idx, scale, out, lse, stream = _prepare(q, k, v, block_idx, scale, out, lse)
     T, Hq, Hkv, nb = q.shape[0], q.shape[1], k.shape[1], block_idx.shape[2]
-    st = lib.qsa_sparse_prefill_blocks(q.data_ptr(), k.data_ptr(), v.data_ptr(), block_idx.data_ptr(), T,
-                                       k.shape[0], int(q_pos0), Hq, Hkv, nb, int(block_size), scale,
-                                       out.data_ptr(), lse.data_ptr(), stream)
+    with _on_device(q.device):
+        st = lib.qsa_sparse_prefill_blocks(q.data_ptr(), k.data_ptr(), v.data_ptr(), block_idx.data_ptr(), T,
+                                           k.shape[0], int(q_pos0), Hq, Hkv, nb, int(block_size), scale,
+                                           out.data_ptr(), lse.data_ptr(), stream)
     _check(st, lib)
     return out, lse
 
@@ -208,9 +219,10 @@ def sparse_prefill_pool(q, k_pool, v_pool, slot_idx, q_pos, slot_pos, scale=None
                                                                     out, lse)
     q_pos, slot_pos = _pool_positions(q, k_pool, q_pos, slot_pos)
     T, Hq, Hkv, K = q.shape[0], q.shape[1], k_pool.shape[1], slot_idx.shape[2]
-    st = lib.qsa_sparse_prefill_pool(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), slot_idx.data_ptr(),
-                                     q_pos.data_ptr(), slot_pos.data_ptr(), T, k_pool.shape[0], Hq, Hkv, K,
-                                     scale, out.data_ptr(), lse.data_ptr(), stream)
+    with _on_device(q.device):
+        st = lib.qsa_sparse_prefill_pool(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), slot_idx.data_ptr(),
+                                         q_pos.data_ptr(), slot_pos.data_ptr(), T, k_pool.shape[0], Hq, Hkv, K,
+                                         scale, out.data_ptr(), lse.data_ptr(), stream)
     _check(st, lib)
     return out, lse
 
@@ -244,8 +256,9 @@ def sparse_decode(q, k_pool, v_pool, slot_idx, q_pos, slot_pos, scale=None, out=
     if not isinstance(workspace, torch.Tensor) or workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the inputs' device")
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.qsa_sparse_decode(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), slot_idx.data_ptr(),
-                               q_pos.data_ptr(), slot_pos.data_ptr(), n_req, k_pool.shape[0], Hq, Hkv, K, scale,
-                               out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), ws_bytes, stream)
+    with _on_device(q.device):
+        st = lib.qsa_sparse_decode(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), slot_idx.data_ptr(),
+                                   q_pos.data_ptr(), slot_pos.data_ptr(), n_req, k_pool.shape[0], Hq, Hkv, K,
+                                   scale, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), ws_bytes, stream)
     _check(st, lib)
     return out, lse

@@ -84,7 +84,9 @@ qsa_status_t sequence_call(const void *q, const void *k, const void *v, const in
                            int32_t block_size, float scale, void *out, float *lse, void *stream) {
     const int shift = log2_block(block_size);
     if (shift < 0) return QSA_ERR_INVALID_ARG;
-    if (q_pos0 < 0 || T_kv < 0 || (T >= 0 && q_pos0 + T > T_kv)) return QSA_ERR_INVALID_ARG;
+    // queries sit at q_pos0 .. q_pos0 + T - 1 and must lie inside the cache
+    // (written without the sum, which could overflow)
+    if (q_pos0 < 0 || T_kv < 0 || q_pos0 > T_kv || (T >= 0 && T > T_kv - q_pos0)) return QSA_ERR_INVALID_ARG;
     const qsa_status_t st = check_common(q, k, v, idx, T, T_kv, Hq, Hkv, n_entries, shift, scale, out, lse);
     if (st != QSA_OK || T == 0) return st;
     return run(make_args(q, k, v, idx, T, T_kv, q_pos0, Hq, Hkv, n_entries, shift, scale, out, lse), stream);
