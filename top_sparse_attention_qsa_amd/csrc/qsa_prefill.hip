@@ -23,7 +23,8 @@
 //      each 16-byte load instruction covers two whole rows, lane l reading
 //      chunk l & 31 of row 2i + (l >> 5), so every quad of lanes reads 64
 //      contiguous bytes and the vector L1 sees whole-line accesses (the row
-//      offsets reach the lanes by DPP row broadcasts). A masked slot gets a
+//      offsets reach the lanes by DPP row broadcasts, or by readlane for
+//      micro-block lists). A masked slot gets a
 //      byte offset past the end of the buffer: the range check returns zeros
 //      and nothing is fetched. The tile goes to registers, then to two padded
 //      LDS tiles (K and V), from which the MFMA operands are read in their
