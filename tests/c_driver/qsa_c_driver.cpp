@@ -1,0 +1,135 @@
+// A plain host program that calls the QSA C ABI (include/qsa.h) with buffers
+// from hipMalloc and a stream of its own: no PyTorch, no Python.
+//
+//   qsa_c_driver <dir>      reads <dir>/meta.txt ("T Hq Hkv K scale"),
+//                           q.bin / k.bin / v.bin (bf16 bits, row-major
+//                           [T,Hq,256] / [T,Hkv,256]) and idx.bin (int32
+//                           [T,Hkv,K]); runs qsa_sparse_prefill; writes
+//                           out.bin (bf16 bits [T,Hq,256]) and lse.bin
+//                           (fp32 [T,Hq]).
+//   qsa_c_driver --selftest checks the ABI version and that invalid
+//                           arguments are refused before any HIP call
+//                           (runs without a GPU).
+//
+// Exit status 0 on success; any failure prints a message and exits 1.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "qsa.h"
+
+namespace {
+
+bool fail(const char *what) {
+    std::fprintf(stderr, "qsa_c_driver: %s\n", what);
+    return false;
+}
+
+bool hip_ok(hipError_t e, const char *what) {
+    if (e == hipSuccess) return true;
+    std::fprintf(stderr, "qsa_c_driver: %s: %s\n", what, hipGetErrorString(e));
+    return false;
+}
+
+template <typename T>
+bool read_file(const std::string &path, std::vector<T> &buf, size_t count) {
+    buf.resize(count);
+    FILE *f = std::fopen(path.c_str(), "rb");
+    if (!f) return fail(("cannot open " + path).c_str());
+    const size_t got = count ? std::fread(buf.data(), sizeof(T), count, f) : 0;
+    std::fclose(f);
+    if (got != count) return fail(("short read of " + path).c_str());
+    return true;
+}
+
+template <typename T>
+bool write_file(const std::string &path, const std::vector<T> &buf) {
+    FILE *f = std::fopen(path.c_str(), "wb");
+    if (!f) return fail(("cannot create " + path).c_str());
+    const size_t put = buf.empty() ? 0 : std::fwrite(buf.data(), sizeof(T), buf.size(), f);
+    std::fclose(f);
+    if (put != buf.size()) return fail(("short write of " + path).c_str());
+    return true;
+}
+
+int selftest() {
+    if (qsa_abi_version() != QSA_ABI_VERSION) return fail("ABI version mismatch"), 1;
+    // Hq not a multiple of Hkv: refused on the host; the pointers are never read
+    static uint16_t dummy[256];
+    static int32_t idx[1];
+    static float lse[3];
+    const qsa_status_t st = qsa_sparse_prefill(dummy, dummy, dummy, idx, 1, 3, 2, 1, 0.0625f, dummy + 8, lse,
+                                               nullptr);
+    if (st != QSA_ERR_INVALID_ARG) return fail("Hq % Hkv != 0 was not refused"), 1;
+    // T == 0 is a no-op with any pointers
+    if (qsa_sparse_prefill(nullptr, nullptr, nullptr, nullptr, 0, 4, 2, 8, 0.0625f, nullptr, nullptr, nullptr) !=
+        QSA_OK)
+        return fail("T == 0 was not a no-op"), 1;
+    std::printf("selftest ok: abi %d, invalid args -> \"%s\"\n", qsa_abi_version(), qsa_status_string(st));
+    return 0;
+}
+
+int run(const std::string &dir) {
+    long long T = 0;
+    int Hq = 0, Hkv = 0, K = 0;
+    float scale = 0.f;
+    {
+        FILE *f = std::fopen((dir + "/meta.txt").c_str(), "r");
+        if (!f) return fail("cannot open meta.txt"), 1;
+        const int n = std::fscanf(f, "%lld %d %d %d %f", &T, &Hq, &Hkv, &K, &scale);
+        std::fclose(f);
+        if (n != 5 || T < 1 || Hq < 1 || Hkv < 1 || K < 0) return fail("bad meta.txt"), 1;
+    }
+    const size_t nq = (size_t)T * Hq * 256, nkv = (size_t)T * Hkv * 256, ni = (size_t)T * Hkv * K;
+    std::vector<uint16_t> q, k, v, out(nq);
+    std::vector<int32_t> idx;
+    std::vector<float> lse((size_t)T * Hq);
+    if (!read_file(dir + "/q.bin", q, nq) || !read_file(dir + "/k.bin", k, nkv) ||
+        !read_file(dir + "/v.bin", v, nkv) || !read_file(dir + "/idx.bin", idx, ni))
+        return 1;
+
+    hipStream_t stream = nullptr;
+    void *dq = nullptr, *dk = nullptr, *dv = nullptr, *di = nullptr, *dout = nullptr, *dlse = nullptr;
+    bool ok = hip_ok(hipStreamCreate(&stream), "hipStreamCreate") &&
+              hip_ok(hipMalloc(&dq, nq * 2), "hipMalloc q") && hip_ok(hipMalloc(&dk, nkv * 2), "hipMalloc k") &&
+              hip_ok(hipMalloc(&dv, nkv * 2), "hipMalloc v") &&
+              hip_ok(hipMalloc(&di, ni * 4 + 4), "hipMalloc idx") &&
+              hip_ok(hipMalloc(&dout, nq * 2), "hipMalloc out") &&
+              hip_ok(hipMalloc(&dlse, lse.size() * 4), "hipMalloc lse") &&
+              hip_ok(hipMemcpyAsync(dq, q.data(), nq * 2, hipMemcpyHostToDevice, stream), "copy q") &&
+              hip_ok(hipMemcpyAsync(dk, k.data(), nkv * 2, hipMemcpyHostToDevice, stream), "copy k") &&
+              hip_ok(hipMemcpyAsync(dv, v.data(), nkv * 2, hipMemcpyHostToDevice, stream), "copy v") &&
+              (ni == 0 || hip_ok(hipMemcpyAsync(di, idx.data(), ni * 4, hipMemcpyHostToDevice, stream), "copy idx"));
+    if (ok) {
+        const qsa_status_t st = qsa_sparse_prefill(dq, dk, dv, (const int32_t *)di, T, Hq, Hkv, K, scale, dout,
+                                                   (float *)dlse, stream);
+        if (st != QSA_OK) {
+            std::fprintf(stderr, "qsa_c_driver: qsa_sparse_prefill: %s\n", qsa_status_string(st));
+            ok = false;
+        }
+    }
+    ok = ok && hip_ok(hipMemcpyAsync(out.data(), dout, nq * 2, hipMemcpyDeviceToHost, stream), "copy out") &&
+         hip_ok(hipMemcpyAsync(lse.data(), dlse, lse.size() * 4, hipMemcpyDeviceToHost, stream), "copy lse") &&
+         hip_ok(hipStreamSynchronize(stream), "hipStreamSynchronize");
+    for (void *p : {dq, dk, dv, di, dout, dlse})
+        if (p) (void)hipFree(p);
+    if (stream) (void)hipStreamDestroy(stream);
+    if (!ok || !write_file(dir + "/out.bin", out) || !write_file(dir + "/lse.bin", lse)) return 1;
+    std::printf("ok: T=%lld Hq=%d Hkv=%d K=%d\n", T, Hq, Hkv, K);
+    return 0;
+}
+
+} // namespace
+
+int main(int argc, char **argv) {
+    if (argc == 2 && std::string(argv[1]) == "--selftest") return selftest();
+    if (argc != 2) {
+        std::fprintf(stderr, "usage: qsa_c_driver <dir> | --selftest\n");
+        return 1;
+    }
+    return run(argv[1]);
+}

@@ -3,7 +3,9 @@
     python -m top_sparse_attention_qsa_amd.build
 
 Compiles every source under csrc/ (HIP kernels and the C ABI shim) into
-top_sparse_attention_qsa_amd/lib/libqsa.so. Always rebuilds.
+top_sparse_attention_qsa_amd/lib/libqsa.so, then the test program
+tests/c_driver/qsa_c_driver.cpp (a plain host program that calls the C ABI)
+into lib/qsa_c_driver, linked against that library. Always rebuilds.
 """
 import os
 import shutil
@@ -16,6 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libqsa.so")
+DRIVER_SRC = os.path.join(ROOT, "tests", "c_driver", "qsa_c_driver.cpp")
+DRIVER = os.path.join(LIB_DIR, "qsa_c_driver")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
@@ -43,10 +47,7 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", INCLUDE, "-I", CSRC, *sources(), "-o", tmp]
+def _run(cmd, verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,7 +57,18 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(LIB_DIR, exist_ok=True)
+    tmp = LIB + ".tmp"
+    _run([hipcc(), *HIP_FLAGS, "-shared", "-I", INCLUDE, "-I", CSRC, *sources(), "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    if os.path.exists(DRIVER_SRC):
+        tmp = DRIVER + ".tmp"
+        _run([hipcc(), *HIP_FLAGS, "-I", INCLUDE, DRIVER_SRC, "-L", LIB_DIR, "-lqsa", "-Wl,-rpath,$ORIGIN",
+              "-o", tmp], verbose)
+        os.replace(tmp, DRIVER)
     return LIB
 
 
