@@ -37,8 +37,9 @@
  * allocation and no per-call state; it enqueues its kernels on `stream` (a
  * hipStream_t, NULL for the null stream) and returns without synchronising.
  * The device that holds the buffers must be the current HIP device, and
- * `stream` must belong to it. Inputs are only read; out and lse must not overlap any input or each other.
- * Calls on different streams may run concurrently.
+ * `stream` must belong to it. Inputs are only read; out and lse must not
+ * overlap any input or each other. Calls on different streams may run
+ * concurrently.
  *
  * Errors: arguments are validated on the host before any HIP call; on error
  * nothing is enqueued and nothing is written. A failed kernel launch returns
@@ -197,6 +198,10 @@ qsa_status_t qsa_sparse_prefill_pool(const void *q, const void *k_pool, const vo
  * Errors as for qsa_sparse_prefill_pool, plus QSA_ERR_INVALID_ARG for a
  * workspace that is needed but NULL, smaller than required, not 16-byte
  * aligned, or equal to another argument's pointer.
+ *
+ * qsa_sparse_decode_workspace_bytes returns -1 for sizes qsa_sparse_decode
+ * would refuse: n_req < 0 or above INT32_MAX, Hq < 1, Hkv < 1,
+ * Hq % Hkv != 0, K < 0 or K > 2^28.
  */
 int64_t qsa_sparse_decode_workspace_bytes(int64_t n_req, int32_t Hq, int32_t Hkv, int32_t K);
 qsa_status_t qsa_sparse_decode(const void *q, const void *k_pool, const void *v_pool, const int32_t *slot_idx,

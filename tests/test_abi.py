@@ -172,7 +172,7 @@ def test_decode_workspace_sizes(lib):
     assert f(127, 24, 2, 2048) == 127 * 24 * 2 * 1040
     assert f(4, 6, 2, 16) == 0                    # one tile: nothing to cut
     assert f(0, 24, 2, 2048) == 0
-    for bad in [(-1, 24, 2, 8), (4, 0, 2, 8), (4, 6, 4, 8), (4, 6, 2, -1), (4, 6, 2, (1 << 28) + 1)]:
+    for bad in [(-1, 24, 2, 8), (2 ** 31, 24, 2, 8), (4, 0, 2, 8), (4, 6, 4, 8), (4, 6, 2, -1), (4, 6, 2, (1 << 28) + 1)]:
         assert f(*bad) == -1
 
 
