@@ -3,7 +3,9 @@
 None of these re-types the oracle's own formula: each compares it with an
 independent library routine (torch's fp64 scaled_dot_product_attention,
 logsumexp, scipy's expit), with a closed form, with an invariant the
-definition implies, or with the pages' own packed-cache identity. The last
+definition implies, with the pages' own packed-cache identity, or with the
+exact value on tiny inputs (50-digit decimal arithmetic, textbook softmax
+without the max shift). The last
 test plants plausible mistakes in the oracle and checks that at least one
 pin catches each of them.
 
@@ -340,6 +342,63 @@ def test_repeated_position_counts_per_entry():
     np.testing.assert_allclose(out[0, 0], p2 * v64[2, 0] + (1 - p2) * v64[5, 0], rtol=0, atol=1e-13)
 
 
+def _decimal_attention(q, k, v, idx, scale, G, digits=50):
+    """Brute force in 50-digit decimal arithmetic, straight from the definition:
+    w_j = exp(z_j) (no max subtracted), out = sum_j w_j v_j / sum_j w_j, lse =
+    ln sum_j w_j. bf16 values and the scale convert to decimal exactly, the
+    products and sums are exact at this precision, and exp / ln are correctly
+    rounded, so the result is the exact value to ~1e-45."""
+    from decimal import Decimal, localcontext
+
+    T, Hq, _ = q.shape
+    q64, k64, v64 = (qo.bf16_to_f64(a) for a in (q, k, v))
+    out = np.zeros((T, Hq, D))
+    lse = np.full((T, Hq), -np.inf)
+    with localcontext() as ctx:
+        ctx.prec = digits
+        sc = Decimal(float(scale))
+        for t in range(T):
+            for h in range(Hq):
+                g = h // G
+                sel = [int(s) for s in idx[t, g] if 0 <= int(s) <= t]
+                if not sel:
+                    continue
+                qd = [Decimal(float(x)) for x in q64[t, h]]
+                w = [(sc * sum(a * Decimal(float(b)) for a, b in zip(qd, k64[s, g]))).exp() for s in sel]
+                l = sum(w)
+                for d in range(D):
+                    out[t, h, d] = float(sum(wi * Decimal(float(v64[s, g, d])) for wi, s in zip(w, sel)) / l)
+                lse[t, h] = float(l.ln())
+    return out, lse
+
+
+def _decimal_case(seed=31):
+    """Tiny rows with shuffled positions, -1 pads, a future position and one
+    repeated position."""
+    rng, q, k, v = _small_case(seed, 7, 4, 2)
+    idx = np.full((7, 2, 6), -1, np.int32)
+    for t in range(7):
+        for g in range(2):
+            row = [int(s) for s in rng.choice(t + 1, size=min(t + 1, 3), replace=False)]
+            row += [row[0], t + 1 + int(rng.integers(0, 4))]
+            row += [-1] * (6 - len(row))
+            rng.shuffle(row)
+            idx[t, g] = row
+    idx[0, 1] = -1  # one empty row
+    return q, k, v, idx
+
+
+def test_tiny_cases_match_decimal_brute_force():
+    q, k, v, idx = _decimal_case()
+    for scale in (1 / 16, 0.3):
+        out, lse = oracle.sparse_prefill(q, k, v, idx, scale=scale)
+        ref_out, ref_lse = _decimal_attention(q, k, v, idx, scale, G=2)
+        np.testing.assert_allclose(out, ref_out, rtol=0, atol=1e-13)
+        np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(ref_lse))
+        fin = np.isfinite(ref_lse)
+        np.testing.assert_allclose(lse[fin], ref_lse[fin], rtol=0, atol=1e-13)
+
+
 def test_bf16_widening_is_exact():
     vals = np.array([0.0, -0.0, 1.0, -2.5, 3.0e38, 1.0e-38, 0.1], np.float32)
     bits = f32_to_bf16_bits(vals)
@@ -388,6 +447,13 @@ def _pin_failures():
     oe, le = oracle.sparse_prefill(q, k, v, empty, scale=1 / 16)
     if not (np.all(oe == 0) and np.all(np.isneginf(le))):
         failures.append("empty_rows")
+    q, k, v, idx = _decimal_case()
+    od, ld = oracle.sparse_prefill(q, k, v, idx, scale=1 / 16)
+    rd, rl = _decimal_attention(q, k, v, idx, 1 / 16, G=2)
+    fin = np.isfinite(rl)
+    if not (np.allclose(od, rd, rtol=0, atol=1e-12) and np.array_equal(np.isfinite(ld), fin)
+            and np.allclose(ld[fin], rl[fin], rtol=0, atol=1e-12)):
+        failures.append("exact_decimal")
     return failures
 
 
