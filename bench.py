@@ -26,7 +26,7 @@ to the one the counters were taken on.
 
 Other workloads (--workload): any of the token workloads c1..c6, the
 micro-block workloads c7/c8 (entries name 4-token blocks, the model's
-compression ratio), the ragged slot-pool batches c9/c10 and the decode
+compression ratio), the ragged slot-pool batches c9/c10/c13 and the decode
 batches c11/c12 (one query per request; the step includes the merge of the
 split lists). Each is timed the same way through its own entry point.
 """
@@ -127,7 +127,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c4", help="c1..c12 or a workload name (default c4)")
+    ap.add_argument("--workload", default="c4", help="c1..c13 or a workload name (default c4)")
     ap.add_argument("--cpu-rows", type=int, default=32768,
                     help="rows for the oracle CPU baseline (all 32,768 rows of the default workload: about 9 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -288,6 +288,16 @@ POOL_CONFIGS: Tuple[PoolConfig, ...] = (
                     "6,144 new; 16,384 empty slots. (24,2), K=2048, 256 window, sink, "
                     "weighted rest",
     ),
+    PoolConfig(
+        name="pool_4req_q32768_slots245760_h24x2_k2048",
+        number=13,
+        requests=tuple(Request(new=8192, cached=49152) for _ in range(4)),
+        Hq=24, Hkv=2, K=2048, window=256, sink=True, sampler="weighted",
+        free_slots=16384, oracle_rows=1024,
+        description="32,768 query tokens in 4 requests of 8,192 new tokens after 49,152 "
+                    "own cached ones each, over a 245,760-slot pool (16,384 empty). "
+                    "(24,2), K=2048, 256 window, sink, weighted rest",
+    ),
 )
 
 

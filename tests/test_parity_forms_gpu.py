@@ -205,9 +205,10 @@ def test_pool_small_workload_all_rows():
     _per_request_extend_bitwise(d, out, lse)
 
 
-def test_pool_full_size_sampled_rows():
+@pytest.mark.parametrize("number", [10, 13])
+def test_pool_full_size_sampled_rows(number):
     t0 = time.perf_counter()
-    d = make_pool_inputs(10)
+    d = make_pool_inputs(number)
     cfg = d["cfg"]
     progress(f"{cfg.name}: inputs in {time.perf_counter() - t0:.1f}s")
     args = (d["q"], d["k"], d["v"], d["idx"], d["q_pos"], d["slot_pos"])
