@@ -10,8 +10,8 @@
 // the G = Hq/Hkv query heads of KV head g (at most 16 per chunk) against the K
 // selected slots of (t, g). Items are independent, so waves never synchronise
 // with each other; a block is WPB such waves, two blocks per CU (one for
-// caches of 80K rows or more, see the launch; split lists use one-wave
-// blocks). Items are numbered KV-head
+// caches of 80K rows or more with 32K items or more, see the launch; split
+// lists use one-wave blocks). Items are numbered KV-head
 // major, and blocks are renumbered so that each XCD (block b runs on XCD
 // b % 8) takes runs of consecutive items: the waves sharing an XCD's L2 hold
 // neighbouring query positions of one KV head, whose local windows, sinks
@@ -569,13 +569,16 @@ __global__ __launch_bounds__(64 * WPB) void qsa_combine_kernel(const float *__re
     if (lane == 0) lse[pair] = empty ? -INFINITY : (M + __log2f(LE)) * kLn2;
 }
 
-// Occupancy by cache length. Two blocks per CU (8 waves) suit caches of up
-// to ~64K rows; from ~96K rows on, one block per CU (4 waves) is 8-15% faster
-// (measured at 98K, 131K and 235K rows, with uniform and with recency-weighted
-// lists), and at 65K rows it is 11% slower to even. The launch reserves extra
-// dynamic LDS that the kernel never touches, so that a second block no longer
-// fits in the CU's 160 KB.
+// Occupancy by cache length and work size. Two blocks per CU (8 waves) suit
+// caches of up to ~64K rows; from ~80K rows on, one block per CU (4 waves) is
+// 5-32% faster once there are at least 32K work items (measured at 82K-235K
+// rows with uniform and recency-weighted lists, and on a 246K-slot pool),
+// while at 65K rows it is 11% slower to even, and with 8K-16K items against a
+// 131K-row cache it is up to 15% slower. The launch reserves extra dynamic LDS
+// that the kernel never touches, so that a second block no longer fits in the
+// CU's 160 KB.
 constexpr uint32_t kOneBlockRows = 81920;
+constexpr int32_t kOneBlockItems = 32768;
 constexpr size_t kLdsPerCu = 160 * 1024;
 
 template <int WPB, int kMode, bool kSplit>
@@ -583,7 +586,8 @@ qsa_status_t launch(const KParams &kp, hipStream_t stream) {
     const uint32_t blocks = (uint32_t)((kp.n_items + WPB - 1) / WPB);
     constexpr size_t kLdsPerBlock = (size_t)WPB * kNK * (kKStride + kVStride);
     static_assert(2 * kLdsPerBlock <= kLdsPerCu, "two blocks must fit for the short-cache case");
-    const size_t pad = (!kSplit && kp.n_rows >= kOneBlockRows) ? kLdsPerCu / 2 + 1024 - kLdsPerBlock : 0;
+    const bool one_block = !kSplit && kp.n_rows >= kOneBlockRows && kp.n_items >= kOneBlockItems;
+    const size_t pad = one_block ? kLdsPerCu / 2 + 1024 - kLdsPerBlock : 0;
     hipLaunchKernelGGL((qsa_prefill_kernel<WPB, kMode, kSplit>), dim3(blocks), dim3(64 * WPB), pad, stream, kp);
     if (hipGetLastError() != hipSuccess) return QSA_ERR_LAUNCH;
     if constexpr (kSplit) {
