@@ -361,3 +361,32 @@ def test_given_output_buffers_and_side_stream():
     assert o.data_ptr() == out.data_ptr() and l.data_ptr() == lse.data_ptr()
     np.testing.assert_array_equal(torch_bf16_to_numpy_bits(out), ref_out)
     np.testing.assert_array_equal(lse.cpu().numpy(), ref_lse)
+
+
+def test_occupancy_modes_give_identical_bits():
+    """The launch runs one or two blocks per CU depending on the cache length
+    and the number of items; the arithmetic of every item is the same either
+    way. The same queries (positions 32,768..65,535) and lists against a
+    98,304-row cache (one block per CU) and against its first 65,536 rows (two
+    blocks; no list reaches past them) give identical bits, for token and for
+    micro-block lists."""
+    rng = np.random.default_rng(91)
+    T, p0, Hq, Hkv, K = 32768, 32768, 4, 1, 48
+    q, k, v = rand_bf16(rng, (T, Hq, 256)), rand_bf16(rng, (98304, Hkv, 256)), rand_bf16(rng, (98304, Hkv, 256))
+    idx = rng.integers(-1, p0 + T, size=(T, Hkv, K)).astype(np.int32)
+    bidx = rng.integers(-1, (p0 + T) // 4, size=(T, Hkv, 16)).astype(np.int32)
+    dq, dk, dv, didx, dbidx = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_i32(idx), dev_i32(bidx)
+    results = {}
+    for rows_kv in (98304, 65536):
+        kk, vv = dk[:rows_kv], dv[:rows_kv]
+        results[rows_kv] = (qsa.sparse_prefill_extend(dq, kk, vv, didx, q_pos0=p0),
+                            qsa.sparse_prefill_blocks(dq, kk, vv, dbidx, p0, 4))
+    torch.cuda.synchronize()
+    for form in (0, 1):
+        (o1, l1), (o2, l2) = results[98304][form], results[65536][form]
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), form
+        assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), form
+    rows = np.array([0, 1, 777, 20000, T - 1])
+    o, l = results[98304][0]
+    ref_out, ref_lse = oracle.sparse_prefill(q, k, v, idx[rows], scale=1 / 16, rows=rows, q_pos0=p0)
+    compare(torch_bf16_to_numpy_bits(o)[rows], l.cpu().numpy()[rows], ref_out, ref_lse, label="one block per CU")
