@@ -10,6 +10,8 @@ prefix, cache reuse).
 As for the token form, nothing here re-types the oracle: full lists reduce to
 dense causal attention, which torch's fp64 scaled_dot_product_attention
 computes independently; single-block and two-slot cases have closed forms;
+tiny block and pool batches are compared with their exact value (50-digit
+decimal arithmetic over the rows the form's rule admits, applied by hand);
 and planted mistakes in the expansion and slot rules must trip a pin.
 """
 import math
@@ -263,6 +265,10 @@ def _form_pin_failures():
         if not (np.allclose(out[a:b], ro, rtol=0, atol=1e-9) and np.allclose(lse[a:b], rl, rtol=0, atol=1e-9)):
             failures.append("pool_full")
             break
+    if not _exact(*_block_decimal_case(), atol=1e-12):
+        failures.append("blocks_exact")
+    if not _exact(*_pool_decimal_case(), atol=1e-12):
+        failures.append("pool_exact")
     return failures
 
 
@@ -338,3 +344,78 @@ def test_decode_batch_is_the_last_row_of_each_requests_attention():
         ro, rl = _sdpa_masked(q[r:r + 1], k[t], v[t], allowed, 1 / 16, G)
         np.testing.assert_allclose(out[r:r + 1], ro, rtol=0, atol=1e-12)
         np.testing.assert_allclose(lse[r:r + 1], rl, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------ exact values
+
+
+def _decimal_over(q, k, v, used, scale, G, digits=50):
+    """Exact attention (50-digit decimal, exp of the raw logits, no max shift)
+    of each query row t and head h over the K/V rows used[t][h // G]."""
+    from decimal import Decimal, localcontext
+
+    T, Hq, _ = q.shape
+    q64, k64, v64 = (qo.bf16_to_f64(a) for a in (q, k, v))
+    out = np.zeros((T, Hq, D))
+    lse = np.full((T, Hq), -np.inf)
+    with localcontext() as ctx:
+        ctx.prec = digits
+        sc = Decimal(float(scale))
+        for t in range(T):
+            for h in range(Hq):
+                sel = used[t][h // G]
+                if not sel:
+                    continue
+                qd = [Decimal(float(x)) for x in q64[t, h]]
+                w = [(sc * sum(a * Decimal(float(b)) for a, b in zip(qd, k64[s, h // G]))).exp() for s in sel]
+                l = sum(w)
+                for d in range(D):
+                    out[t, h, d] = float(sum(wi * Decimal(float(v64[s, h // G, d])) for wi, s in zip(w, sel)) / l)
+                lse[t, h] = float(l.ln())
+    return out, lse
+
+
+def _block_decimal_case():
+    """Micro-block lists (block size 4, a cached prefix, the query's own block
+    cut at the query, -1 and out-of-range entries, an empty row) and their
+    exact value, the token rule applied by hand: entry b names tokens
+    4b..4b+3, each used iff it is at or before the query's position."""
+    rng = np.random.default_rng(61)
+    T, p0, Hq, Hkv, B = 5, 9, 4, 2, 4
+    T_kv = p0 + T
+    q, k, v = _rand_bf16(rng, (T, Hq, D)), _rand_bf16(rng, (T_kv, Hkv, D)), _rand_bf16(rng, (T_kv, Hkv, D))
+    idx = rng.integers(-1, T_kv // B + 2, size=(T, Hkv, 5)).astype(np.int32)
+    idx[2, 1] = -1
+    used = [[[b * B + i for b in idx[t, g] if b >= 0 for i in range(B) if b * B + i <= p0 + t]
+             for g in range(Hkv)] for t in range(T)]
+    out, lse = oracle.sparse_prefill_blocks(q, k, v, idx, B, scale=1 / 16, q_pos0=p0)
+    return (out, lse) + _decimal_over(q, k, v, used, 1 / 16, G=Hq // Hkv)
+
+
+def _pool_decimal_case():
+    """A pool batch (permuted slots, a shared prefix, empty slots, slots past
+    the pool, a request's own later tokens) and its exact value, the slot
+    rule applied by hand: slot s is used iff it is inside the pool, holds a
+    token, and that token's position is at or before the query's."""
+    rng, tables, slot_pos, k, v, _, G = _two_request_pool(62)
+    n_slots = slot_pos.size
+    q, idx, q_pos, _ = _pool_batch(rng, tables, slot_pos, 4, {"A": 2, "B": 2, "C": 1}, 48,
+                                   _pool_masked_extra(tables, slot_pos, n_slots))
+    used = [[[int(s) for s in idx[r, g] if 0 <= s < n_slots and 0 <= slot_pos[s] <= q_pos[r]]
+             for g in range(idx.shape[1])] for r in range(q.shape[0])]
+    out, lse = oracle.sparse_prefill_pool(q, k, v, idx, q_pos, slot_pos, scale=1 / 16)
+    return (out, lse) + _decimal_over(q, k, v, used, 1 / 16, G=G)
+
+
+def _exact(out, lse, ref_out, ref_lse, atol):
+    fin = np.isfinite(ref_lse)
+    return (np.allclose(out, ref_out, rtol=0, atol=atol) and np.array_equal(np.isfinite(lse), fin)
+            and np.allclose(lse[fin], ref_lse[fin], rtol=0, atol=atol))
+
+
+def test_block_lists_match_decimal_brute_force():
+    assert _exact(*_block_decimal_case(), atol=1e-13)
+
+
+def test_pool_lists_match_decimal_brute_force():
+    assert _exact(*_pool_decimal_case(), atol=1e-13)
