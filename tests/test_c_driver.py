@@ -26,6 +26,19 @@ def test_selftest_runs_without_a_gpu():
     assert "selftest ok" in res.stdout
 
 
+def test_abi_validation_under_host_sanitizers():
+    """The C ABI's argument validation (tests/c_driver/qsa_abi_sanitize.cpp,
+    built with g++ -fsanitize=address,undefined and a stub launch) over the
+    extremes of every argument and a seeded random mix: no undefined
+    behaviour, and every accepted call meets the kernels' preconditions."""
+    if not os.path.exists(qsa_build.SANITIZE):
+        pytest.fail("qsa_abi_sanitize is not built: run __graft_entry__.build() first")
+    env = dict(os.environ, ASAN_OPTIONS="verify_asan_link_order=0:detect_leaks=0")
+    res = subprocess.run([qsa_build.SANITIZE], capture_output=True, text=True, timeout=300, env=env)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert " 0 invariant violations" in res.stdout
+
+
 def ragged_case(seed=2024, T=300, Hq=12, Hkv=2, K=100):
     """T spans several 16-slot tiles with a ragged tail; lists are unordered
     with -1 pads and future positions mixed in."""

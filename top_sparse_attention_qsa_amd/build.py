@@ -5,7 +5,9 @@
 Compiles every source under csrc/ (HIP kernels and the C ABI shim) into
 top_sparse_attention_qsa_amd/lib/libqsa.so, then the test program
 tests/c_driver/qsa_c_driver.cpp (a plain host program that calls the C ABI)
-into lib/qsa_c_driver, linked against that library. Always rebuilds.
+into lib/qsa_c_driver, linked against that library, and, with g++, the host
+check tests/c_driver/qsa_abi_sanitize.cpp (the ABI's validation under ASan
+and UBSan) into lib/qsa_abi_sanitize. Always rebuilds.
 """
 import os
 import shutil
@@ -20,6 +22,8 @@ LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libqsa.so")
 DRIVER_SRC = os.path.join(ROOT, "tests", "c_driver", "qsa_c_driver.cpp")
 DRIVER = os.path.join(LIB_DIR, "qsa_c_driver")
+SANITIZE_SRC = os.path.join(ROOT, "tests", "c_driver", "qsa_abi_sanitize.cpp")
+SANITIZE = os.path.join(LIB_DIR, "qsa_abi_sanitize")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
@@ -69,6 +73,14 @@ def build(verbose: bool = False) -> str:
         _run([hipcc(), *HIP_FLAGS, "-I", INCLUDE, DRIVER_SRC, "-L", LIB_DIR, "-lqsa", "-Wl,-rpath,$ORIGIN",
               "-o", tmp], verbose)
         os.replace(tmp, DRIVER)
+    gxx = shutil.which("g++")
+    if os.path.exists(SANITIZE_SRC) and gxx:
+        # host code only: the C-ABI validation under ASan/UBSan with a stub launch
+        tmp = SANITIZE + ".tmp"
+        _run([gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+              "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I", INCLUDE, "-I", CSRC,
+              os.path.join(CSRC, "qsa_api.cpp"), SANITIZE_SRC, "-o", tmp], verbose)
+        os.replace(tmp, SANITIZE)
     return LIB
 
 

@@ -104,7 +104,7 @@ SplitPlan plan_split(int64_t T, int32_t Hq, int32_t Hkv, int32_t K_slots) {
     // are only cut when the unsplit launch has fewer than 256 waves.
     constexpr int64_t kTargetWaves = 512;
     const int64_t n_tiles = ((int64_t)K_slots + 15) / 16;
-    const int64_t items = T * Hkv * ((Hq / Hkv + 15) / 16);
+    const int64_t items = T * Hkv * (((int64_t)Hq / Hkv + 15) / 16);
     if (n_tiles <= 1 || items >= kTargetWaves / 2) return {1, (int32_t)n_tiles};
     int64_t tps = (n_tiles * items + kTargetWaves - 1) / kTargetWaves;
     if (tps < 1) tps = 1;

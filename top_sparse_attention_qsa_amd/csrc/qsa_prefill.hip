@@ -616,7 +616,7 @@ qsa_status_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     kp.Hq = a.Hq;
     kp.Hkv = a.Hkv;
     kp.G = a.Hq / a.Hkv;
-    kp.n_hchunks = (kp.G + 15) / 16;
+    kp.n_hchunks = (int32_t)(((int64_t)kp.G + 15) / 16);
     kp.K_idx = a.K;
     kp.blk_shift = a.blk_shift;
     kp.K_slots = a.K << a.blk_shift;
