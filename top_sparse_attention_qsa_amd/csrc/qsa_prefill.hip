@@ -427,7 +427,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
                 sl.spos = __builtin_amdgcn_raw_buffer_load_b32(rp, sl.ok ? (uint32_t)e * 4u : kOob, 0, 0);
                 return sl.ok ? (uint32_t)e * row_stride + head_off : kOob;
             } else {
-                const int32_t s = (e << shift) | sub;
+                const int32_t s = (int32_t)(((uint32_t)e << shift) | (uint32_t)sub); // used only if e <= bmax
                 const bool ok = in_list && e >= 0 && e <= bmax && (int64_t)s <= tq;
                 sl.mask = (uint32_t)__ballot(ok) & 0xFFFFu;
                 return ok ? (uint32_t)s * row_stride + head_off : kOob;
