@@ -250,6 +250,96 @@ def test_pool_masks_free_outside_and_future_slots():
     compare(out, lse, ref_out, ref_lse, label="pool masking")
 
 
+# bf16 bit patterns that must never reach an output through a masked slot:
+# quiet NaN, NaN with a payload, +Inf, -Inf, negative NaN
+NON_FINITE_BF16 = np.array([0x7FC0, 0x7F81, 0x7F80, 0xFF80, 0xFFC0], np.uint16)
+
+
+def _poison(rng, shape):
+    return NON_FINITE_BF16[rng.integers(0, NON_FINITE_BF16.size, size=shape)]
+
+
+def _poisoned_pool(seed):
+    """A pool whose free slots and whose slots holding tokens after every
+    query of their request hold NaN / Inf rows in K and V, with lists that
+    name those slots among valid ones. Free slots are normal in a reused KV
+    pool, and a pool may already hold a request's later tokens (the pages'
+    tests of physical slot mappings and cache reuse, "Qwen4-Exp QSA llega al
+    Ascend de Huawei", section "Nueve pruebas que pasaron"). Request A holds
+    positions 0..199 with queries at 100..149 (positions 150..199 poisoned);
+    request B holds positions 0..99 with queries at 60..99; 100 free slots."""
+    rng = np.random.default_rng(seed)
+    n_a, n_b, n_free, Hkv, Hq, K = 200, 100, 100, 2, 8, 96
+    n_slots = n_a + n_b + n_free
+    perm = rng.permutation(n_slots)
+    table_a, table_b, free = perm[:n_a], perm[n_a:n_a + n_b], perm[n_a + n_b:]
+    slot_pos = np.full(n_slots, -1, np.int32)
+    slot_pos[table_a] = np.arange(n_a)
+    slot_pos[table_b] = np.arange(n_b)
+    k, v = rand_bf16(rng, (n_slots, Hkv, 256)), rand_bf16(rng, (n_slots, Hkv, 256))
+    bad = np.concatenate([free, table_a[150:]])
+    k[bad] = _poison(rng, (bad.size, Hkv, 256))
+    v[bad] = _poison(rng, (bad.size, Hkv, 256))
+    queries = [(p, table_a) for p in range(100, 150)] + [(p, table_b) for p in range(60, 100)]
+    q = rand_bf16(rng, (len(queries), Hq, 256))
+    q_pos = np.array([p for p, _ in queries], np.int32)
+    idx = np.full((len(queries), Hkv, K), -1, np.int32)
+    for i, (p, table) in enumerate(queries):
+        for g in range(Hkv):
+            own = list(rng.choice(table[: p + 1], size=min(p + 1, 60), replace=False))
+            later = list(table[p + 1: p + 12]) + (list(rng.choice(table_a[150:], 6, replace=False))
+                                                  if table is table_a else [])
+            junk = list(rng.choice(free, 10, replace=False)) + [n_slots, n_slots + 5, -1, INT32_MIN]
+            row = own + later + junk
+            rng.shuffle(row)
+            idx[i, g, : len(row)] = row
+    return q, k, v, idx, q_pos, slot_pos
+
+
+def test_pool_and_decode_never_read_masked_slots():
+    """NaN / Inf in slots that the slot rule masks (free slots, tokens after
+    the query) leave every output finite and equal to the oracle's, which
+    never looks at them: such slots are not gathered at all."""
+    q, k, v, idx, q_pos, slot_pos = _poisoned_pool(17)
+    ref_out, ref_lse = oracle.sparse_prefill_pool(q, k, v, idx, q_pos, slot_pos)
+    assert np.all(np.isfinite(ref_out)) and np.all(np.isfinite(ref_lse))
+    out, lse = run_pool(q, k, v, idx, q_pos, slot_pos)
+    compare(out, lse, ref_out, ref_lse, label="pool, poisoned masked slots")
+    # decode: one query per request (the last one of each), lists cut into ranges
+    last = np.array([49, q.shape[0] - 1])
+    assert qsa.decode_workspace_bytes(2, q.shape[1], k.shape[1], idx.shape[2]) > 0
+    out, lse = run_decode(q[last], k, v, idx[last], q_pos[last], slot_pos)
+    compare(out, lse, ref_out[last], ref_lse[last], label="decode, poisoned masked slots")
+
+
+def test_sequence_forms_never_read_masked_rows():
+    """Token and micro-block lists naming cache rows after the query, whose K
+    and V hold NaN / Inf: every output finite and equal to the oracle's."""
+    rng = np.random.default_rng(18)
+    T, p0, T_kv, Hq, Hkv = 64, 100, 300, 6, 2
+    q = rand_bf16(rng, (T, Hq, 256))
+    k, v = rand_bf16(rng, (T_kv, Hkv, 256)), rand_bf16(rng, (T_kv, Hkv, 256))
+    k[p0 + T:] = _poison(rng, (T_kv - p0 - T, Hkv, 256))
+    v[p0 + T:] = _poison(rng, (T_kv - p0 - T, Hkv, 256))
+    idx = np.full((T, Hkv, 80), -1, np.int32)
+    bidx = np.full((T, Hkv, 24), -1, np.int32)
+    for t in range(T):
+        pos = p0 + t
+        for g in range(Hkv):
+            row = list(rng.choice(pos + 1, 50, replace=False)) + list(rng.integers(pos + 1, T_kv, 20))
+            rng.shuffle(row)
+            idx[t, g, : len(row)] = row
+            brow = list(rng.choice(pos // 4 + 1, 16, replace=False)) + list(rng.integers(pos // 4 + 1, T_kv // 4, 8))
+            rng.shuffle(brow)
+            bidx[t, g] = brow
+    out, lse = run_tokens(q, k, v, idx, q_pos0=p0)
+    ref_out, ref_lse = oracle.sparse_prefill(q, k, v, idx, scale=1 / 16, q_pos0=p0)
+    compare(out, lse, ref_out, ref_lse, label="tokens, poisoned later rows")
+    out, lse = run_blocks(q, k, v, bidx, 4, q_pos0=p0)
+    ref_out, ref_lse = oracle.sparse_prefill_blocks(q, k, v, bidx, 4, scale=1 / 16, q_pos0=p0)
+    compare(out, lse, ref_out, ref_lse, label="blocks, poisoned later rows")
+
+
 def test_pool_cache_reuse_and_inputs_unchanged():
     """The same batch twice over the same pool buffers: identical outputs,
     inputs untouched (cache content reused, never written)."""

@@ -54,7 +54,9 @@
 // j+1 and V of tile j go out spread over the stores rather than as a burst
 // that would fill the texture unit's queues), then issues the score MFMAs of
 // tile j and finishes tile j-1; the two are independent, so the MFMAs run
-// under the softmax. Indices run three tiles ahead of the scores.
+// under the softmax. Indices run three tiles ahead of the scores; in pool
+// form the positions of the listed slots run two tiles ahead, so that a slot
+// its position masks (free, or holding a later token) is never gathered.
 //
 // Split lists (decode). With one query per request there are too few items
 // to fill the chip, so each item's list can be cut into n_splits ranges of
@@ -343,6 +345,8 @@ __device__ __forceinline__ void tile_finish(f32x4_t s, const uint8_t *lv, uint32
 //            used under the same rule;
 //   kPool    entries are slots of a K/V pool; slot s is used iff
 //            0 <= s < n_rows and 0 <= slot_pos[s] <= q_pos[row].
+// In every form a slot that is not used gets no row offset: its K/V row is
+// never read, whatever it holds.
 enum IndexForm { kTokens = 0, kBlocks = 1, kPool = 2 };
 
 template <int WPB, int kMode, bool kSplit>
@@ -410,34 +414,38 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
         uint8_t *lk = &lds_k[w][0];
         uint8_t *lv = &lds_v[w][0];
 
-        // Row byte offset of this lane's slot in tile j (kOob when it cannot
-        // be used: the range check then returns zeros and fetches nothing),
-        // and what decides the tile's validity mask (bit k = key k): in the
-        // sequence forms the mask itself, taken here; in pool form the slot's
-        // token position, loaded here and tested when the tile is consumed.
-        struct Slot {
-            uint32_t mask;
-            bool ok;
-            int32_t spos;
-        };
-        auto prep = [&](int j, int32_t e, Slot &sl) -> uint32_t {
-            const bool in_list = j * kNK + hl < slot_end;
+        // Pool form: the position of the token held by pool slot e (read as 0
+        // for an entry outside the pool, which the slot test masks anyway).
+        // It is loaded one iteration before the slot's tile forms its row
+        // offsets, so a slot that its position masks (a free slot, a token
+        // after the query) is never gathered: its row may hold anything,
+        // NaN included, and contributes nothing.
+        auto load_spos = [&](int32_t e) -> int32_t {
             if constexpr (kIsPool) {
-                sl.ok = in_list && e >= 0 && (uint32_t)e < p.n_rows;
-                sl.spos = __builtin_amdgcn_raw_buffer_load_b32(rp, sl.ok ? (uint32_t)e * 4u : kOob, 0, 0);
-                return sl.ok ? (uint32_t)e * row_stride + head_off : kOob;
+                const bool in_pool = e >= 0 && (uint32_t)e < p.n_rows;
+                return __builtin_amdgcn_raw_buffer_load_b32(rp, in_pool ? (uint32_t)e * 4u : kOob, 0, 0);
             } else {
-                const int32_t s = (int32_t)(((uint32_t)e << shift) | (uint32_t)sub); // used only if e <= bmax
-                const bool ok = in_list && e >= 0 && e <= bmax && (int64_t)s <= tq;
-                sl.mask = (uint32_t)__ballot(ok) & 0xFFFFu;
-                return ok ? (uint32_t)s * row_stride + head_off : kOob;
+                return 0;
             }
         };
-        auto tile_mask = [&](const Slot &sl) -> uint32_t {
-            if constexpr (kIsPool)
-                return (uint32_t)__ballot(sl.ok && sl.spos >= 0 && (int64_t)sl.spos <= tq) & 0xFFFFu;
-            else
-                return sl.mask;
+        // Row byte offset of this lane's slot in tile j, entry e (pool form:
+        // slot position spos), or kOob when the slot cannot be used (the range
+        // check then returns zeros and fetches nothing); `mask` gets the
+        // tile's validity bits (bit k = key k).
+        auto prep = [&](int j, int32_t e, int32_t spos, uint32_t &mask) -> uint32_t {
+            const bool in_list = j * kNK + hl < slot_end;
+            bool ok;
+            uint32_t off;
+            if constexpr (kIsPool) {
+                ok = in_list && e >= 0 && (uint32_t)e < p.n_rows && spos >= 0 && (int64_t)spos <= tq;
+                off = (uint32_t)e * row_stride + head_off;
+            } else {
+                const int32_t s = (int32_t)(((uint32_t)e << shift) | (uint32_t)sub); // used only if e <= bmax
+                ok = in_list && e >= 0 && e <= bmax && (int64_t)s <= tq;
+                off = (uint32_t)s * row_stride + head_off;
+            }
+            mask = (uint32_t)__ballot(ok) & 0xFFFFu;
+            return ok ? off : kOob;
         };
 
         // Software pipeline, one tile deep: iteration j writes K of tile j
@@ -446,14 +454,16 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
         // weighted values). The two halves are independent, so the MFMAs of
         // one overlap the vector work of the other. Loads past the range are
         // masked (nothing fetched); the loop runs one iteration past the last
-        // tile to finish it.
+        // tile to finish it. Pool slot positions run two tiles ahead.
         u32x4_t ks[8], vs[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) vs[i] = (u32x4_t){0u, 0u, 0u, 0u};
-        Slot cur, nxt;
         int32_t i0 = load_tile_idx(ri, j_begin, shift, lane);
         int32_t inext = load_tile_idx(ri, j_begin + 1, shift, lane);
-        uint32_t off_cur = prep(j_begin, i0, cur);
+        const int32_t sp0 = load_spos(i0);
+        int32_t sp_next = load_spos(inext);
+        uint32_t mask_cur;
+        uint32_t off_cur = prep(j_begin, i0, sp0, mask_cur);
         {
             const TileOffsets t0 = tile_offsets<kRlOffsets>(off_cur, lane);
 #pragma unroll
@@ -463,18 +473,19 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2))
         f32x4_t s_prev = {0.f, 0.f, 0.f, 0.f};
         uint32_t mask_prev = 0;
         for (int j = j_begin;; ++j) {
-            const uint32_t off_next = prep(j + 1, inext, nxt);
+            uint32_t mask_next;
+            const uint32_t off_next = prep(j + 1, inext, sp_next, mask_next);
+            sp_next = load_spos(inext2); // tile j+2
             rotate_tiles(lk, lv, rk, rv, tile_offsets<kRlOffsets>(off_next, lane),
                          tile_offsets<kRlOffsets>(off_cur, lane), ks, vs, lane);
             inext = inext2;
             inext2 = load_tile_idx(ri, j + 3, shift, lane);
-            const uint32_t mask = tile_mask(cur);
             const f32x4_t sc = tile_scores(lk, qb, lane);
             if (mask_prev) tile_finish(s_prev, lv, mask_prev, o, st, p.scale_log2, lane);
             if (j >= j_end) break;
             s_prev = sc;
-            mask_prev = mask;
-            cur = nxt;
+            mask_prev = mask_cur;
+            mask_cur = mask_next;
             off_cur = off_next;
         }
     }
