@@ -209,6 +209,37 @@ qsa_status_t qsa_sparse_decode(const void *q, const void *k_pool, const void *v_
                                int32_t Hq, int32_t Hkv, int32_t K, float scale, void *out, float *lse,
                                void *workspace, int64_t workspace_bytes, void *stream);
 
+/*
+ * qsa_sparse_decode_noalloc -- qsa_sparse_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same operation, kernels and results,
+ * bit for bit, with the split partials in a scratch array that the library
+ * holds in device memory instead of a caller's workspace. The call allocates
+ * nothing.
+ *
+ * The scratch is QSA_DECODE_SCRATCH_BYTES (16 MiB) per GPU, held from the
+ * library's load until the process ends; the first call on a device looks up
+ * that device's copy. Every valid size fits it: the split plan never needs
+ * more than about 12.8 MB (at most 16 * 767 partial rows of 1,040 bytes).
+ * Every call on one GPU shares that GPU's scratch, so calls that overlap on
+ * one GPU (e.g. on two streams at once) race and give undefined results;
+ * calls ordered on one stream are safe. Nothing in the scratch needs to
+ * start at zero: each call writes every partial it reads.
+ *
+ *   arguments as for qsa_sparse_decode, without workspace / workspace_bytes
+ *
+ * Errors as for qsa_sparse_decode (minus the workspace checks), plus
+ * QSA_ERR_UNSUPPORTED if a split plan ever needed more than
+ * QSA_DECODE_SCRATCH_BYTES (no valid size does) or the current device
+ * number is 64 or higher, and QSA_ERR_LAUNCH if the HIP runtime cannot give
+ * the scratch's device address.
+ */
+#define QSA_DECODE_SCRATCH_BYTES (16LL << 20)
+qsa_status_t qsa_sparse_decode_noalloc(const void *q, const void *k_pool, const void *v_pool,
+                                       const int32_t *slot_idx, const int32_t *q_pos, const int32_t *slot_pos,
+                                       int64_t n_req, int64_t n_slots, int32_t Hq, int32_t Hkv, int32_t K,
+                                       float scale, void *out, float *lse, void *stream);
+
 /* Static, NUL-terminated description of a status code ("unknown status" otherwise). */
 const char *qsa_status_string(qsa_status_t status);
 

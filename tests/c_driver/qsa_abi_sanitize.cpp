@@ -5,7 +5,9 @@
 // The kernels are not linked: qsa::launch_prefill is replaced by a stub that
 // receives every call the validation lets through and checks the invariants
 // the kernels rely on (sizes in range, no 32-bit offset overflow, the pointers
-// that will be read present, query positions inside the cache). Pointers are
+// that will be read present, query positions inside the cache, split
+// partials that fit the no-allocation decode's scratch), and
+// qsa::device_scratch by one that returns a fake address. Pointers are
 // never dereferenced, so fake non-null values are safe here. Every entry point
 // is driven over the extremes of each argument and over a seeded random mix.
 //
@@ -22,6 +24,7 @@
 namespace {
 
 long g_launches = 0;
+long g_scratch_lookups = 0;
 long g_failures = 0;
 bool g_sequence_call = false; // the current call is a sequence form (not pool)
 
@@ -61,7 +64,15 @@ qsa_status_t launch_prefill(const PrefillArgs &a, hipStream_t) {
         check(a.pool && a.workspace != nullptr && ((uintptr_t)a.workspace & 15u) == 0, "workspace");
         check(a.tiles_per_split >= 1, "tiles per range");
         check((int64_t)a.n_splits * a.tiles_per_split * 16 >= ((int64_t)a.K << a.blk_shift), "ranges cover the list");
+        check(a.T * a.Hq * a.n_splits * 1040 <= QSA_DECODE_SCRATCH_BYTES, "split partials fit the static scratch");
     }
+    return QSA_OK;
+}
+
+// the no-allocation decode's scratch: a fake, 256-byte aligned device address
+qsa_status_t device_scratch(void **ptr) {
+    ++g_scratch_lookups;
+    *ptr = (void *)(uintptr_t)0x20000000u;
     return QSA_OK;
 }
 
@@ -108,6 +119,7 @@ void call_all(int64_t T, int64_t T_kv, int64_t q_pos0, int32_t Hq, int32_t Hkv, 
     const int64_t need = qsa_sparse_decode_workspace_bytes(T, Hq, Hkv, K);
     const int64_t have = (int64_t)(next() % 3 == 0 ? 0 : (need > 0 ? need : 16));
     (void)qsa_sparse_decode(q, k, v, idx, qp, sp, T, T_kv, Hq, Hkv, K, scale, out, lse, ws, have, nullptr);
+    (void)qsa_sparse_decode_noalloc(q, k, v, idx, qp, sp, T, T_kv, Hq, Hkv, K, scale, out, lse, nullptr);
 }
 
 } // namespace
@@ -154,6 +166,11 @@ int main() {
         std::fprintf(stderr, "no call was accepted: the harness exercised nothing\n");
         return 1;
     }
-    std::printf("%ld accepted calls checked, %ld invariant violations\n", g_launches, g_failures);
+    if (g_scratch_lookups == 0) {
+        std::fprintf(stderr, "no no-allocation decode call needed its scratch: the harness exercised nothing\n");
+        return 1;
+    }
+    std::printf("%ld accepted calls checked (%ld scratch lookups), %ld invariant violations\n", g_launches,
+                g_scratch_lookups, g_failures);
     return g_failures == 0 ? 0 : 1;
 }

@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    assert names == ["qsa_abi_version", "qsa_sparse_decode", "qsa_sparse_decode_workspace_bytes",
+    assert names == ["qsa_abi_version", "qsa_sparse_decode", "qsa_sparse_decode_noalloc",
+                     "qsa_sparse_decode_workspace_bytes",
                      "qsa_sparse_prefill", "qsa_sparse_prefill_blocks", "qsa_sparse_prefill_extend",
                      "qsa_sparse_prefill_pool", "qsa_status_string"]
 
@@ -186,3 +187,47 @@ def test_decode_workspace_sizes(lib):
 ])
 def test_decode_argument_rules(lib, kwargs, expect):
     assert call_dec(lib, **kwargs) == expect
+
+
+DECODE_SCRATCH_BYTES = 16 << 20  # QSA_DECODE_SCRATCH_BYTES in include/qsa.h
+
+
+def test_header_states_the_scratch_size():
+    assert re.search(r"#define QSA_DECODE_SCRATCH_BYTES \(16LL << 20\)", open(HEADER).read())
+
+
+def test_every_decode_plan_fits_the_static_scratch(lib):
+    """The no-allocation decode keeps its partials in a 16 MiB scratch: the
+    workspace of every split plan fits it (the bound is 16 * 767 rows of
+    1,040 bytes), over request counts up to the no-split limit, head groups
+    of 1..48 (several 16-head chunks included) and list widths up to 2^28."""
+    f = lib.qsa_sparse_decode_workspace_bytes
+    worst = 0
+    for n_req in list(range(1, 40)) + [63, 64, 85, 100, 127, 128, 200, 255, 256, 300]:
+        for Hkv in (1, 2, 3, 4, 8):
+            for G in (1, 3, 6, 8, 12, 16, 17, 24, 32, 48):
+                for K in (17, 64, 2048, 2051, 65536, 1 << 20, 1 << 28):
+                    need = f(n_req, Hkv * G, Hkv, K)
+                    assert 0 <= need <= DECODE_SCRATCH_BYTES, (n_req, Hkv, G, K, need)
+                    worst = max(worst, need)
+    assert worst > DECODE_SCRATCH_BYTES // 2  # the sweep reaches near the bound
+
+
+def call_noalloc(lib, n_req=16, n_slots=1000, Hq=24, Hkv=2, K=2048, scale=0.0625, q_pos=QP, slot_pos=SP, out=OUT,
+                 lse=LSE, idx=IDX, q=Q):
+    return lib.qsa_sparse_decode_noalloc(q, K_, V, idx, q_pos, slot_pos, n_req, n_slots, Hq, Hkv, K, scale, out,
+                                         lse, None)
+
+
+@pytest.mark.parametrize("kwargs,expect", [
+    (dict(n_req=-1), INVALID), (dict(n_req=2 ** 31), INVALID), (dict(q_pos=None), INVALID),
+    (dict(slot_pos=None), INVALID), (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(lse=None), INVALID),
+    (dict(idx=None), INVALID), (dict(out=QP), INVALID), (dict(lse=SP), INVALID), (dict(Hq=6, Hkv=4), INVALID),
+    (dict(Hq=0), INVALID), (dict(K=-1), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(n_slots=4194304, Hkv=1, Hq=1), UNSUPPORTED), (dict(K=(1 << 28) + 1), UNSUPPORTED),
+    (dict(n_req=0), OK), (dict(n_req=0, q_pos=None, slot_pos=None), OK),
+])
+def test_decode_noalloc_argument_rules(lib, kwargs, expect):
+    """The no-allocation decode validates like qsa_sparse_decode, on the
+    host, before its first HIP call (none of these calls reaches a device)."""
+    assert call_noalloc(lib, **kwargs) == expect

@@ -22,6 +22,7 @@ __all__ = [
     "sparse_prefill_blocks",
     "sparse_prefill_pool",
     "sparse_decode",
+    "sparse_decode_noalloc",
     "decode_workspace_bytes",
     "load_library",
     "library_path",
@@ -78,6 +79,9 @@ def load_library(path: str = None):
     lib.qsa_sparse_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_float, vp, vp,
                                       vp, i64, vp]
     lib.qsa_sparse_decode.restype = ctypes.c_int
+    lib.qsa_sparse_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_float, vp,
+                                              vp, vp]
+    lib.qsa_sparse_decode_noalloc.restype = ctypes.c_int
     lib.qsa_status_string.argtypes = [ctypes.c_int]
     lib.qsa_status_string.restype = ctypes.c_char_p
     lib.qsa_abi_version.argtypes = []
@@ -260,5 +264,26 @@ def sparse_decode(q, k_pool, v_pool, slot_idx, q_pos, slot_pos, scale=None, out=
         st = lib.qsa_sparse_decode(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), slot_idx.data_ptr(),
                                    q_pos.data_ptr(), slot_pos.data_ptr(), n_req, k_pool.shape[0], Hq, Hkv, K,
                                    scale, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), ws_bytes, stream)
+    _check(st, lib)
+    return out, lse
+
+
+def sparse_decode_noalloc(q, k_pool, v_pool, slot_idx, q_pos, slot_pos, scale=None, out=None, lse=None):
+    """sparse_decode with the split partials in the library's own device
+    scratch (16 MiB per GPU, held until the process ends) instead of a
+    workspace: the library call allocates no memory. Results are bit-identical
+    to sparse_decode. Calls that overlap on one GPU (two streams at once) race
+    on the scratch; calls on one stream are safe. Pass `out` and `lse` to keep
+    the whole call free of allocation (this binding allocates them otherwise)."""
+    lib = load_library()
+    q, k_pool, v_pool, slot_idx, scale, out, lse, stream = _prepare(q, k_pool, v_pool, slot_idx, scale,
+                                                                    out, lse)
+    q_pos, slot_pos = _pool_positions(q, k_pool, q_pos, slot_pos)
+    n_req, Hq, Hkv, K = q.shape[0], q.shape[1], k_pool.shape[1], slot_idx.shape[2]
+    with _on_device(q.device):
+        st = lib.qsa_sparse_decode_noalloc(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                           slot_idx.data_ptr(), q_pos.data_ptr(), slot_pos.data_ptr(), n_req,
+                                           k_pool.shape[0], Hq, Hkv, K, scale, out.data_ptr(), lse.data_ptr(),
+                                           stream)
     _check(st, lib)
     return out, lse

@@ -92,6 +92,30 @@ qsa_status_t sequence_call(const void *q, const void *k, const void *v, const in
     return run(make_args(q, k, v, idx, T, T_kv, q_pos0, Hq, Hkv, n_entries, shift, scale, out, lse), stream);
 }
 
+// Checks of the decode entry points up to the workspace, and the call they
+// make: `a` gets the arguments and split plan, `need` the workspace bytes the
+// plan uses (0: no split). QSA_OK with n_req == 0 means nothing to do.
+qsa_status_t decode_args(const void *q, const void *k_pool, const void *v_pool, const int32_t *slot_idx,
+                         const int32_t *q_pos, const int32_t *slot_pos, int64_t n_req, int64_t n_slots, int32_t Hq,
+                         int32_t Hkv, int32_t K, float scale, void *out, float *lse, qsa::PrefillArgs &a,
+                         int64_t &need) {
+    const qsa_status_t st =
+        check_common(q, k_pool, v_pool, slot_idx, n_req, n_slots, Hq, Hkv, K, 0, scale, out, lse);
+    if (st != QSA_OK || n_req == 0) return st;
+    if (q_pos == nullptr || (slot_pos == nullptr && n_slots > 0)) return QSA_ERR_INVALID_ARG;
+    if (aliases(out, lse, {(const void *)q_pos, (const void *)slot_pos})) return QSA_ERR_INVALID_ARG;
+    const qsa::SplitPlan plan = qsa::plan_split(n_req, Hq, Hkv, K);
+    need = qsa::split_workspace_bytes(n_req, Hq, plan);
+    a = make_args(q, k_pool, v_pool, slot_idx, n_req, n_slots, 0, Hq, Hkv, K, 0, scale, out, lse);
+    a.pool = true;
+    a.q_pos = q_pos;
+    a.slot_pos = slot_pos;
+    a.n_splits = plan.n_splits;
+    a.tiles_per_split = plan.tiles_per_split;
+    a.workspace = nullptr;
+    return QSA_OK;
+}
+
 } // namespace
 
 namespace qsa {
@@ -113,7 +137,10 @@ SplitPlan plan_split(int64_t T, int32_t Hq, int32_t Hkv, int32_t K_slots) {
 
 int64_t split_workspace_bytes(int64_t T, int32_t Hq, const SplitPlan &plan) {
     if (plan.n_splits <= 1) return 0;
-    // per (row, head, range): a 16-byte (m, l, le) record and 256 fp32 of O
+    // per (row, head, range): a 16-byte (m, l, le) record and 256 fp32 of O.
+    // Bounded for every size: a split happens only with items <= 255, each
+    // item holds at most 16 heads, and n_splits <= 512 / items + 1, so there
+    // are at most 16 * (512 + 255) partial rows (12.8 MB).
     return T * Hq * plan.n_splits * (16 + 256 * 4);
 }
 
@@ -170,28 +197,38 @@ qsa_status_t qsa_sparse_decode(const void *q, const void *k_pool, const void *v_
                                const int32_t *q_pos, const int32_t *slot_pos, int64_t n_req, int64_t n_slots,
                                int32_t Hq, int32_t Hkv, int32_t K, float scale, void *out, float *lse,
                                void *workspace, int64_t workspace_bytes, void *stream) {
-    const qsa_status_t st =
-        check_common(q, k_pool, v_pool, slot_idx, n_req, n_slots, Hq, Hkv, K, 0, scale, out, lse);
+    qsa::PrefillArgs a;
+    int64_t need = 0;
+    qsa_status_t st = decode_args(q, k_pool, v_pool, slot_idx, q_pos, slot_pos, n_req, n_slots, Hq, Hkv, K, scale,
+                                  out, lse, a, need);
     if (st != QSA_OK || n_req == 0) return st;
-    if (q_pos == nullptr || (slot_pos == nullptr && n_slots > 0) || workspace_bytes < 0)
-        return QSA_ERR_INVALID_ARG;
-    if (aliases(out, lse, {(const void *)q_pos, (const void *)slot_pos, workspace})) return QSA_ERR_INVALID_ARG;
-    const qsa::SplitPlan plan = qsa::plan_split(n_req, Hq, Hkv, K);
-    const int64_t need = qsa::split_workspace_bytes(n_req, Hq, plan);
+    if (workspace_bytes < 0 || aliases(out, lse, {workspace})) return QSA_ERR_INVALID_ARG;
     if (need > 0) {
         if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 15u) != 0)
             return QSA_ERR_INVALID_ARG;
         for (const void *in : {q, k_pool, v_pool, (const void *)slot_idx, (const void *)q_pos,
                                (const void *)slot_pos})
             if (in == workspace) return QSA_ERR_INVALID_ARG;
+        a.workspace = workspace;
     }
-    qsa::PrefillArgs a = make_args(q, k_pool, v_pool, slot_idx, n_req, n_slots, 0, Hq, Hkv, K, 0, scale, out, lse);
-    a.pool = true;
-    a.q_pos = q_pos;
-    a.slot_pos = slot_pos;
-    a.n_splits = plan.n_splits;
-    a.tiles_per_split = plan.tiles_per_split;
-    a.workspace = need > 0 ? workspace : nullptr;
+    return run(a, stream);
+}
+
+qsa_status_t qsa_sparse_decode_noalloc(const void *q, const void *k_pool, const void *v_pool,
+                                       const int32_t *slot_idx, const int32_t *q_pos, const int32_t *slot_pos,
+                                       int64_t n_req, int64_t n_slots, int32_t Hq, int32_t Hkv, int32_t K,
+                                       float scale, void *out, float *lse, void *stream) {
+    qsa::PrefillArgs a;
+    int64_t need = 0;
+    qsa_status_t st = decode_args(q, k_pool, v_pool, slot_idx, q_pos, slot_pos, n_req, n_slots, Hq, Hkv, K, scale,
+                                  out, lse, a, need);
+    if (st != QSA_OK || n_req == 0) return st;
+    if (need > QSA_DECODE_SCRATCH_BYTES) return QSA_ERR_UNSUPPORTED;
+    if (need > 0) {
+        // the first HIP call of this entry point: every argument is checked
+        st = qsa::device_scratch(&a.workspace);
+        if (st != QSA_OK) return st;
+    }
     return run(a, stream);
 }
 

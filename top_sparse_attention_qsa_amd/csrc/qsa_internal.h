@@ -48,4 +48,8 @@ int64_t split_workspace_bytes(int64_t T, int32_t Hq, const SplitPlan &plan);
 // Enqueue the operator on `stream`. Arguments are already validated and T > 0.
 qsa_status_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
+// Device address of the current device's QSA_DECODE_SCRATCH_BYTES scratch
+// array (looked up on the first call per device, then cached).
+qsa_status_t device_scratch(void **ptr);
+
 } // namespace qsa

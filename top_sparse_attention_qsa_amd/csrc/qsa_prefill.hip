@@ -77,6 +77,9 @@
 
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 namespace qsa {
 namespace {
 
@@ -659,6 +662,43 @@ qsa_status_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     }
     if (a.pool) return launch<4, kPool, false>(kp, stream);
     return a.blk_shift ? launch<4, kBlocks, false>(kp, stream) : launch<4, kTokens, false>(kp, stream);
+}
+
+} // namespace qsa
+
+// Scratch of qsa_sparse_decode_noalloc: the split partials of one decode call
+// ((m, l, le) records, then fp32 partial rows), in device memory that the
+// library holds from its load until the process ends, one copy per GPU. In
+// host code `scratch` names a host-side stand-in, not device memory: kernels
+// and copies get the address from device_scratch below.
+static __device__ __align__(256) uint8_t scratch[QSA_DECODE_SCRATCH_BYTES];
+
+namespace qsa {
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+} // namespace
+
+qsa_status_t device_scratch(void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return QSA_ERR_LAUNCH;
+    if (dev >= kMaxDevices) return QSA_ERR_UNSUPPORTED;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            // with device `dev` current: that device's copy of the array
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+                (void)hipGetLastError(); // do not leave the error for the caller's next HIP call
+                return QSA_ERR_LAUNCH;
+            }
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return QSA_OK;
 }
 
 } // namespace qsa
