@@ -129,7 +129,7 @@ CONFIGS: Tuple[Config, ...] = (
         number=3,
         T=32768, Hq=16, Hkv=2, K=2048,
         window=256, sink=True, gap=0, sampler="weighted",
-        outlier_frac=0.01, outlier_scale=8.0, oracle_rows=4096,
+        outlier_frac=0.01, outlier_scale=8.0, oracle_rows=0,
         description="T=32768, (16,2), K=2048: 256-token window, sink 0, rest with "
                     "weight 1/(1+(t-s)/1024), independent per KV head; 1% of "
                     "positions have K and V rows scaled x8",
@@ -139,7 +139,7 @@ CONFIGS: Tuple[Config, ...] = (
         number=4,
         T=32768, Hq=24, Hkv=2, K=2048,
         window=256, sink=True, gap=0, sampler="weighted",
-        oracle_rows=4096,
+        oracle_rows=0,
         description="T=32768, (24,2), K=2048: as the (16,2) workload without "
                     "outliers; 12 query heads per KV head",
     ),
@@ -162,7 +162,7 @@ EXTEND_CONFIG = Config(
     number=6,
     T=7810, Hq=12, Hkv=1, K=2051,
     window=512, sink=True, gap=0, sampler="uniform",
-    oracle_rows=512, q_pos0=65536 - 7810, T_kv=65536,
+    oracle_rows=0, q_pos0=65536 - 7810, T_kv=65536,
     description="7,810 queries at positions 57,726..65,535 against a 65,536-token "
                 "K/V cache, (12,1), K=2051: 512-token window, sink 0, uniform rest",
 )
@@ -185,7 +185,7 @@ BLOCK_CONFIGS: Tuple[Config, ...] = (
         number=8,
         T=32768, Hq=24, Hkv=2, K=2048,
         window=64, sink=True, gap=0, sampler="weighted", block_size=4,
-        oracle_rows=512,
+        oracle_rows=4096,
         description="T=32768, (24,2), 2,048 micro-blocks of 4 tokens (8,192 token "
                     "slots): 64-block window ending at the query's block, block 0, "
                     "rest weighted 1/(1+(b_t-b)/1024), independent per KV head",
@@ -281,7 +281,7 @@ POOL_CONFIGS: Tuple[PoolConfig, ...] = (
         requests=(Request(new=12288), Request(new=8192, cached=8192, share_from=0),
                   Request(new=6144, cached=16384), Request(new=6144)),
         Hq=24, Hkv=2, K=2048, window=256, sink=True, sampler="weighted",
-        free_slots=16384, oracle_rows=1024,
+        free_slots=16384, oracle_rows=0,
         description="32,768 query tokens in 4 requests over a 65,536-slot pool: "
                     "12,288 new; 8,192 new after the first 8,192 tokens of the first "
                     "request (shared slots); 6,144 new after 16,384 own cached; "
@@ -293,7 +293,7 @@ POOL_CONFIGS: Tuple[PoolConfig, ...] = (
         number=13,
         requests=tuple(Request(new=8192, cached=49152) for _ in range(4)),
         Hq=24, Hkv=2, K=2048, window=256, sink=True, sampler="weighted",
-        free_slots=16384, oracle_rows=1024,
+        free_slots=16384, oracle_rows=0,
         description="32,768 query tokens in 4 requests of 8,192 new tokens after 49,152 "
                     "own cached ones each, over a 245,760-slot pool (16,384 empty). "
                     "(24,2), K=2048, 256 window, sink, weighted rest",

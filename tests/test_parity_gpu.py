@@ -113,7 +113,10 @@ def test_workload_all_rows(number):
 
 
 @pytest.mark.parametrize("number", [3, 4, 5, 6])
-def test_workload_full_size_sampled_rows(number):
+def test_workload_full_size(number):
+    """The full-size workloads, checked on every row (the two T = 32,768
+    workloads and the extend workload) or on 4,096 seeded rows plus the
+    edge rows (the 235,008-token workload); every output finite."""
     cfg = get_config(number)
     t0 = time.perf_counter()
     progress(f"{cfg.name}: generating inputs ({oracle_pool.default_workers()} workers, "
@@ -122,7 +125,8 @@ def test_workload_full_size_sampled_rows(number):
     progress(f"{cfg.name}: q/k/v in {time.perf_counter() - t0:.1f}s")
     idx = make_indices(cfg)
     progress(f"{cfg.name}: idx in {time.perf_counter() - t0:.1f}s")
-    rows = sample_rows(cfg, n=min(cfg.oracle_rows, 4096 if number == 5 else 1024))
+    rows = sample_rows(cfg)
+    assert rows.size == (4096 + 6 if number == 5 else cfg.T)
     out, lse, stats = check(q, k, v, idx, scale=cfg.scale, rows=rows, q_pos0=cfg.q_pos0, label=cfg.name)
     g = out.view(np.uint16)
     # every output finite (bf16 exponent not all ones) and every row non-empty
