@@ -13,16 +13,24 @@ Default workload: T = 32768 query tokens, (Hq, Hkv) = (24, 2) -- the
 section "Por qué QSA es la parte incómoda, en cifras" -- K = 2048 selected
 slots per (token, KV head) (the page's 2,048 budget), head dim 256, bf16.
 
-Roofline: the kernel is bound by HBM bandwidth on the gathered rows. Per
-valid slot it must gather 512 B of K and 512 B of V; `achieved` is those
-algorithmic bytes per launch divided by the mean kernel duration, measured
-with a HIP event pair around the K timed steps on the stream the kernel runs
-on, against MI355X's 8 TB/s. A second pass of K steps, each between its own
-events, gives the minimum and median launch durations.
-`traffic` comes from committed rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs
-of this same command, scaled by the counters' reading on a copy kernel of
-known size, and is reported only while the built library is byte-identical
-to the one the counters were taken on.
+Roofline: the operator is a gather (G <= 12 flop per gathered byte against a
+ridge of ~310), and every gathered byte reaches the waves through the
+vector-memory return path: L2 (16 channels x 128 B/clk per XCD, 8 XCDs) to
+the vector L1 and the texture-data unit of each CU (64 B/clk, 256 CUs), both
+16 KiB per clock chip-wide, 39.3 TB/s at the 2.4 GHz peak clock. Most
+gathered rows repeat across neighbouring queries and are served from L2, so
+that path, not HBM, binds the cache-resident workloads. `achieved` is the
+algorithmic bytes per launch (512 B of K + 512 B of V per valid slot) over
+the mean kernel duration, measured with a HIP event pair around the K timed
+steps on the stream the kernel runs on. A second pass of K steps, each
+between its own events, gives the minimum and median launch durations.
+`traffic` is what crosses L2 to the fabric per launch (Infinity Cache hits
+and HBM), from committed rocprofv3 counter runs of this same command: reads
+from the L2's own request counts by size (32, 64 and 128 B), writes from
+WRITE_SIZE; `past_l2` sets it against the 8 TB/s HBM peak. Both are reported
+only while the built library is byte-identical to the one the counters were
+taken on. `hbm_roofline_frac` is the metric's logical figure (gathered bytes
+over 8 TB/s): above 1 whenever caches serve the gather, so not a roofline.
 
 Other workloads (--workload): any of the token workloads c1..c6, the
 micro-block workloads c7/c8 (entries name 4-token blocks, the model's
@@ -41,6 +49,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# L2 -> CU return path: 8 XCDs x 16 L2 channels x 128 B per clock (= 256 CUs x
+# 64 B per clock into the texture-data units) at the 2.4 GHz peak clock
+L2_CU_BYTES_PER_CLK = 8 * 16 * 128
+PEAK_CLOCK_HZ = 2.4e9
+L2_CU_PEAK_GBPS = L2_CU_BYTES_PER_CLK * PEAK_CLOCK_HZ / 1e9
 LIBRARY = "top_sparse_attention_qsa_amd/lib/libqsa.so"
 METRIC = "QSA sparse prefill query-tokens/s and gathered-KV GB/s (% HBM roofline), 1 GPU"
 
@@ -59,17 +72,53 @@ def log(msg):
 
 
 def measured_traffic(workload: str, sha: str):
-    """Bytes per launch moved past L2 (FETCH_SIZE + WRITE_SIZE, calibrated), from the
-    committed counter summary of this workload, or None when absent or stale."""
+    """Counter record of this workload's kernel (bytes per launch past L2, the
+    clock under load) from its committed summary, or None when absent or
+    taken on another build of the library."""
     path = os.path.join(ROOT, "profiles", f"qsa_prefill_kernel_{workload}_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_sha") != sha:
+    if not rec or rec.get("kernel_sha") != sha or "read_bytes_per_launch" not in rec:
         return None
-    return int(round(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]))
+    return rec
+
+
+def roofline_records(gathered: int, kernel_s: float, counters):
+    """The `roofline` and `past_l2` objects for `gathered` algorithmic bytes
+    per launch and a mean launch of `kernel_s` seconds; `counters` is the
+    workload's counter record (measured_traffic) or None."""
+    achieved = gathered / kernel_s / 1e9
+    traffic = None if counters is None else int(round(counters["read_bytes_per_launch"]
+                                                      + counters["write_bytes_per_launch"]))
+    roofline = {
+        "bound": "l2",
+        "bound_detail": "vector-memory return path: L2 (8 XCDs x 16 channels x 128 B/clk) to the CUs' "
+                        "vector L1 / texture-data units (256 x 64 B/clk) = 16 KiB/clk at 2.4 GHz; every "
+                        "gathered K/V byte crosses it",
+        "achieved": round(achieved, 1),
+        "peak": round(L2_CU_PEAK_GBPS, 1),
+        "unit": "GB/s",
+        "frac": round(achieved / L2_CU_PEAK_GBPS, 4),
+        "traffic": traffic,
+        "traffic_kind": "bytes per launch from L2 to the fabric (Infinity Cache hits and HBM), reads from "
+                        "the L2's 32/64/128-B request counts, writes from WRITE_SIZE",
+        "kernel": "qsa_prefill_kernel",
+        "algorithmic_bytes_per_launch": gathered,
+    }
+    if counters is not None and counters.get("clock_hz"):
+        # the same fraction at the clock the counters measured under this load
+        clk = counters["clock_hz"]
+        roofline["profiled_clock_GHz"] = round(clk / 1e9, 3)
+        roofline["frac_at_profiled_clock"] = round(achieved / (L2_CU_BYTES_PER_CLK * clk / 1e9), 4)
+    past_l2 = None
+    if traffic is not None:
+        past_l2 = {"bytes_per_launch": traffic, "GBps": round(traffic / kernel_s / 1e9, 1),
+                   "frac_of_hbm_peak": round(traffic / kernel_s / 1e9 / HBM_PEAK_GBPS, 4),
+                   "gathered_bytes_from_l2_frac": round(1 - counters["read_bytes_per_launch"] / gathered, 4)}
+    return roofline, past_l2
 
 
 def load_inputs(cfg):
@@ -96,15 +145,18 @@ def cpu_baseline(cfg, d, n_rows: int):
         kw = {"q_pos0": cfg.q_pos0, "block_size": cfg.block_size if cfg.block_size > 1 else None}
     rows = rows[:n_rows]
     workers = pool.default_workers()
+    affinity = pool.affinity_cpus()
     _, _, secs = pool.run_rows(d["q"], d["k"], d["v"], d["idx"][rows], rows, cfg.scale, workers=workers,
                                return_seconds=True, **kw)
     return {
         "value": round(float(rows.size / secs), 3),
         "unit": "query-tokens/s",
         "cores": workers,
+        "affinity_cpus": affinity,
         "kind": "oracle",
         "sample": f"{rows.size} seeded rows of {cfg.name} (all {cfg.Hq} heads each), fp64 NumPy, "
-                  f"one process per core, BLAS single-threaded; {secs:.2f} s wall",
+                  f"{workers} processes (one per core; {affinity} CPUs in this process's affinity set, "
+                  f"at most {pool.MAX_WORKERS} used), BLAS single-threaded; {secs:.2f} s wall",
     }
 
 
@@ -207,6 +259,7 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
     cold0, cold1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     cold0.record(stream)
     step()
@@ -245,8 +298,14 @@ def main():
     kernel_s = region_ms * 1e-3
     achieved = gathered / kernel_s / 1e9
     sha = kernel_sha()
-    traffic = measured_traffic(cfg.name, sha)
+    counters = measured_traffic(cfg.name, sha)
     qtok_s = cfg.T / (ms_per_step * 1e-3)
+    logical_gbps = gathered / (ms_per_step * 1e-3) / 1e9
+
+    roofline, past_l2 = roofline_records(gathered, kernel_s, counters)
+    roofline.update(kernel_ms_mean=round(region_ms, 4), kernel_ms_min=round(float(kms.min()), 4),
+                    kernel_ms_median=round(float(np.median(kms)), 4),
+                    kernel_ms_mean_per_launch_pass=round(float(kms.mean()), 4), kernel_sha=sha)
 
     res = {
         "metric": METRIC,
@@ -262,27 +321,18 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": workload_config(cfg),
-        "gathered_kv_GBps": round(gathered / (ms_per_step * 1e-3) / 1e9, 1),
-        "hbm_roofline_frac": round(gathered / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "copy_roofline_frac": round(gathered / (ms_per_step * 1e-3) / 1e9 / copy_gbps, 4),
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "kernel": "qsa_prefill_kernel",
-            "algorithmic_bytes_per_launch": gathered,
-            "kernel_ms_mean": round(region_ms, 4),
-            "kernel_ms_min": round(float(kms.min()), 4),
-            "kernel_ms_median": round(float(np.median(kms)), 4),
-            "kernel_ms_mean_per_launch_pass": round(float(kms.mean()), 4),
-            "kernel_sha": sha,
-        },
+        "gathered_kv_GBps": round(logical_gbps, 1),
+        "hbm_roofline_frac": round(logical_gbps / HBM_PEAK_GBPS, 4),
+        "copy_roofline_frac": round(logical_gbps / copy_gbps, 4),
+        "roofline": roofline,
+        "past_l2": past_l2,
         "first_call_ms": round(first_ms, 3),
         "copy_GBps": round(copy_gbps, 1),
         "useful_tflops": round(cfg.useful_flops() / kernel_s / 1e12, 2),
+        "device_memory": {"max_allocated_bytes": int(torch.cuda.max_memory_allocated(dev)),
+                          "max_allocated_MiB": round(torch.cuda.max_memory_allocated(dev) / 2 ** 20, 1),
+                          "note": "PyTorch allocator peak over the timed calls: resident inputs, outputs "
+                                  "and any decode workspace; the library itself allocates nothing"},
         "cpu_baseline": cpu,
         "gpu_over_cpu": round(qtok_s / cpu["value"], 1) if cpu else None,
     }

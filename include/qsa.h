@@ -37,9 +37,12 @@
  * allocation and no per-call state; it enqueues its kernels on `stream` (a
  * hipStream_t, NULL for the null stream) and returns without synchronising.
  * The device that holds the buffers must be the current HIP device, and
- * `stream` must belong to it. Inputs are only read; out and lse must not
- * overlap any input or each other. Calls on different streams may run
- * concurrently.
+ * `stream` must belong to it; it is typed void * so that this header needs
+ * no HIP include (pass a hipStream_t unchanged). Inputs are only read; out
+ * and lse must not overlap any input or each other: the library rejects an
+ * out or lse pointer equal to an input's (or to each other) but does not
+ * detect partial overlaps, whose results are undefined. Calls on different
+ * streams may run concurrently.
  *
  * Errors: arguments are validated on the host before any HIP call; on error
  * nothing is enqueued and nothing is written. A failed kernel launch returns

@@ -22,12 +22,21 @@ from . import qsa_oracle
 _ARRAYS = {}
 
 
-def default_workers() -> int:
+# Worker processes are capped at 16: one GPU's share of a multi-GPU host's
+# cores, whatever the process's affinity set shows.
+MAX_WORKERS = 16
+
+
+def affinity_cpus() -> int:
+    """CPUs in this process's affinity set."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        return os.cpu_count() or 1
+
+
+def default_workers() -> int:
+    return max(1, min(MAX_WORKERS, affinity_cpus()))
 
 
 def _init(paths):

@@ -38,17 +38,45 @@ def test_workload_records_are_complete(cfg):
 def test_traffic_only_for_the_profiled_library(tmp_path, monkeypatch):
     prof = tmp_path / "profiles"
     prof.mkdir()
-    rec = {"kernel_sha": "abc", "fetch_bytes_per_launch": 1000.4, "write_bytes_per_launch": 20.2}
+    rec = {"kernel_sha": "abc", "read_bytes_per_launch": 1000.4, "write_bytes_per_launch": 20.2,
+           "clock_hz": 2.2e9}
     (prof / "qsa_prefill_kernel_w_traffic.json").write_text(json.dumps(rec))
+    (prof / "qsa_prefill_kernel_old_traffic.json").write_text(json.dumps(
+        {"kernel_sha": "abc", "fetch_bytes_per_launch": 1.0, "write_bytes_per_launch": 2.0}))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    assert bench.measured_traffic("w", "abc") == 1021
+    assert bench.measured_traffic("w", "abc") == rec
     assert bench.measured_traffic("w", "abd") is None
     assert bench.measured_traffic("other", "abc") is None
+    assert bench.measured_traffic("old", "abc") is None  # a record without request-size read bytes
+
+
+def test_roofline_is_the_l2_return_path():
+    """Gathered bytes over the L2 -> CU return path's peak (16 KiB per clock at
+    2.4 GHz), with past-L2 traffic set against the HBM peak."""
+    assert bench.L2_CU_PEAK_GBPS == pytest.approx(39321.6)
+    gathered, secs = 133_146_083_328, 5.9e-3
+    roof, past = bench.roofline_records(gathered, secs, None)
+    assert roof["bound"] == "l2" and roof["unit"] == "GB/s" and past is None and roof["traffic"] is None
+    assert roof["achieved"] == pytest.approx(gathered / secs / 1e9, abs=0.1)
+    assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], abs=1e-4) and 0 < roof["frac"] < 1
+    rec = {"read_bytes_per_launch": 11.0e9, "write_bytes_per_launch": 0.4e9, "clock_hz": 2.14e9}
+    roof, past = bench.roofline_records(gathered, secs, rec)
+    assert roof["traffic"] == 11_400_000_000
+    assert roof["frac_at_profiled_clock"] == pytest.approx(gathered / secs / (16384 * 2.14e9), abs=1e-4)
+    assert past["GBps"] == pytest.approx(11.4e9 / secs / 1e9, abs=0.1)
+    assert past["frac_of_hbm_peak"] == pytest.approx(11.4e9 / secs / 8e12, abs=1e-4)
 
 
 def test_committed_profiles_name_their_library():
     for name in os.listdir(os.path.join(ROOT, "profiles")):
         if name.endswith("_traffic.json"):
             rec = json.load(open(os.path.join(ROOT, "profiles", name)))
-            assert len(rec["kernel_sha"]) == 16 and rec["fetch_bytes_per_launch"] > 0
+            assert len(rec["kernel_sha"]) == 16
+            assert rec.get("read_bytes_per_launch", rec.get("fetch_bytes_per_launch", 0)) > 0
             assert all("bench.py" in c for c in rec["commands"])
+
+
+def test_oracle_worker_count_is_reported():
+    from oracle import pool
+    assert 1 <= pool.default_workers() <= pool.MAX_WORKERS
+    assert pool.default_workers() <= pool.affinity_cpus()
