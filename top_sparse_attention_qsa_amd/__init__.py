@@ -95,12 +95,45 @@ def _check(status: int, lib) -> None:
         raise QsaError(status, lib.qsa_status_string(status).decode())
 
 
+class _OnDevice:
+    """Make device `index` the current HIP device for the call (the library
+    launches on the given stream with whatever device is current); no device
+    switch at all when it is current already, the common case."""
+
+    __slots__ = ("index", "prev")
+
+    def __init__(self, index):
+        self.index = index
+        self.prev = None
+
+    def __enter__(self):
+        import torch
+
+        cur = torch.cuda.current_device()
+        if cur != self.index:
+            torch.cuda.set_device(self.index)
+            self.prev = cur
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            import torch
+
+            torch.cuda.set_device(self.prev)
+        return False
+
+
 def _on_device(dev):
-    """Make `dev` the current HIP device for the call (the library launches on
-    the given stream with whatever device is current)."""
+    return _OnDevice(dev.index)
+
+
+def _current_stream(dev) -> int:
+    """Raw HIP stream handle of the current stream of `dev`."""
     import torch
 
-    return torch.cuda.device(dev)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(dev.index)
+    return torch.cuda.current_stream(dev).cuda_stream
 
 
 def _prepare(q, k, v, idx, scale, out, lse):
@@ -140,8 +173,7 @@ def _prepare(q, k, v, idx, scale, out, lse):
         raise ValueError("out must be a contiguous bf16 [T, Hq, 256] tensor on the inputs' device")
     if lse.shape != (T, Hq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != dev:
         raise ValueError("lse must be a contiguous fp32 [T, Hq] tensor on the inputs' device")
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    return q, k, v, idx, scale, out, lse, stream
+    return q, k, v, idx, scale, out, lse, _current_stream(dev)
 
 
 def sparse_prefill(q, k, v, idx, scale=None, out=None, lse=None):
