@@ -256,22 +256,6 @@ def main():
     torch.cuda.synchronize()
     copy_gbps = 2 * copy_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
-    # the same copy on a buffer the L2s hold (16 MiB in + 16 MiB out against
-    # 8 x 4 MB of L2), repeated: what a plain streaming kernel gets from L2
-    l2_bytes, l2_reps = 16 << 20, 200
-    src = torch.empty(l2_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
-    dst = torch.empty_like(src)
-    for _ in range(20):
-        torch.mul(src, 1.0, out=dst)
-    torch.cuda.synchronize()
-    c0.record()
-    for _ in range(l2_reps):
-        torch.mul(src, 1.0, out=dst)
-    c1.record()
-    torch.cuda.synchronize()
-    l2_copy_gbps = 2 * l2_bytes * l2_reps / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del src, dst
-
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats(dev)
@@ -343,7 +327,6 @@ def main():
         "past_l2": past_l2,
         "first_call_ms": round(first_ms, 3),
         "copy_GBps": round(copy_gbps, 1),
-        "l2_resident_copy_GBps": round(l2_copy_gbps, 1),
         "useful_tflops": round(cfg.useful_flops() / kernel_s / 1e12, 2),
         "device_memory": {"max_allocated_bytes": int(torch.cuda.max_memory_allocated(dev)),
                           "max_allocated_MiB": round(torch.cuda.max_memory_allocated(dev) / 2 ** 20, 1),
