@@ -55,6 +55,10 @@ L2_CU_BYTES_PER_CLK = 8 * 16 * 128
 PEAK_CLOCK_HZ = 2.4e9
 L2_CU_PEAK_GBPS = L2_CU_BYTES_PER_CLK * PEAK_CLOCK_HZ / 1e9
 LIBRARY = "top_sparse_attention_qsa_amd/lib/libqsa.so"
+PROBE = "top_sparse_attention_qsa_amd/lib/qsa_gather_probe"
+# the library's occupancy rule: one 4-wave block per CU for caches of 81,920
+# rows or more with 32,768 work items or more, two blocks otherwise
+ONE_BLOCK_ROWS, ONE_BLOCK_ITEMS = 81920, 32768
 METRIC = "QSA sparse prefill query-tokens/s and gathered-KV GB/s (% HBM roofline), 1 GPU"
 
 
@@ -119,6 +123,47 @@ def roofline_records(gathered: int, kernel_s: float, counters):
                    "frac_of_hbm_peak": round(traffic / kernel_s / 1e9 / HBM_PEAK_GBPS, 4),
                    "gathered_bytes_from_l2_frac": round(1 - counters["read_bytes_per_launch"] / gathered, 4)}
     return roofline, past_l2
+
+
+def kernel_waves_per_cu(cfg):
+    """Waves per CU the gather kernel runs this workload with (None for the
+    decode batches, whose split ranges run in one-wave blocks)."""
+    from qsa_inputs import PoolConfig
+
+    if isinstance(cfg, PoolConfig):
+        if cfg.decode:
+            return None
+        n_rows = cfg.n_slots
+    else:
+        n_rows = cfg.kv_len
+    items = cfg.T * cfg.Hkv * ((cfg.Hq // cfg.Hkv + 15) // 16)
+    return 4 if n_rows >= ONE_BLOCK_ROWS and items >= ONE_BLOCK_ITEMS else 8
+
+
+def parse_probe(text: str):
+    """GB/s from the gather probe's output line, or None."""
+    import re
+
+    m = re.search(r"([\d.]+) TB/s", text)
+    return float(m.group(1)) * 1000.0 if m else None
+
+
+def measure_gather_ceiling(waves_per_cu: int):
+    """The gather probe on L2-resident rows (8,192 rows of 512 B) at the
+    kernel's waves per CU, 16 loads in flight per wave (16 KB, as the kernel
+    holds): GB/s received by the waves, median of 5 launches; None when the
+    probe is not built or fails."""
+    import subprocess
+
+    path = os.path.join(ROOT, PROBE)
+    if waves_per_cu is None or not os.path.exists(path):
+        return None
+    try:
+        res = subprocess.run([path, "8192", str(waves_per_cu), "200", "16", "5"], capture_output=True, text=True,
+                             timeout=120)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    return parse_probe(res.stdout) if res.returncode == 0 else None
 
 
 def load_inputs(cfg):
@@ -256,6 +301,11 @@ def main():
     torch.cuda.synchronize()
     copy_gbps = 2 * copy_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
+    # what this GPU delivers to the waves for random 512-B rows held in L2, at
+    # the kernel's occupancy (a separate process, before the timed region)
+    wpc = kernel_waves_per_cu(cfg)
+    ceiling = measure_gather_ceiling(wpc)
+
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats(dev)
@@ -302,6 +352,11 @@ def main():
     logical_gbps = gathered / (ms_per_step * 1e-3) / 1e9
 
     roofline, past_l2 = roofline_records(gathered, kernel_s, counters)
+    if ceiling:
+        roofline["measured_ceiling"] = {
+            "GBps": round(ceiling, 1), "waves_per_cu": wpc, "frac": round(achieved / ceiling, 4),
+            "what": "qsa_gather_probe in this run: random 512-B row pairs from an L2-resident 4 MB buffer, the "
+                    "kernel's load shape and waves per CU, 16 loads in flight per wave, no other work"}
     roofline.update(kernel_ms_mean=round(region_ms, 4), kernel_ms_min=round(float(kms.min()), 4),
                     kernel_ms_median=round(float(np.median(kms)), 4),
                     kernel_ms_mean_per_launch_pass=round(float(kms.mean()), 4), kernel_sha=sha)

@@ -80,3 +80,24 @@ def test_oracle_worker_count_is_reported():
     from oracle import pool
     assert 1 <= pool.default_workers() <= pool.MAX_WORKERS
     assert pool.default_workers() <= pool.affinity_cpus()
+
+
+def test_kernel_occupancy_rule():
+    """bench.py mirrors the library's launch rule to run the gather probe at
+    the kernel's waves per CU: one 4-wave block per CU for caches of 81,920
+    rows or more with 32,768 items or more."""
+    from qsa_inputs import get_config
+    waves = {n: bench.kernel_waves_per_cu(get_config(n)) for n in range(1, 14)}
+    assert waves[4] == waves[3] == waves[10] == waves[8] == waves[6] == 8
+    assert waves[5] == waves[13] == 4
+    assert waves[11] is None and waves[12] is None
+    src = open(os.path.join(ROOT, "top_sparse_attention_qsa_amd", "csrc", "qsa_prefill.hip")).read()
+    assert f"kOneBlockRows = {bench.ONE_BLOCK_ROWS};" in src
+    assert f"kOneBlockItems = {bench.ONE_BLOCK_ITEMS};" in src
+
+
+def test_probe_output_is_parsed():
+    line = ("gather probe: rows 8192 (4.2 MB), 8 waves/CU, 16 loads in flight per wave (128 KB per CU): "
+            "median 1.086 ms of 5, 24.72 TB/s\n")
+    assert bench.parse_probe(line) == pytest.approx(24720.0)
+    assert bench.parse_probe("nothing") is None

@@ -83,3 +83,17 @@ def test_plain_host_program_matches_binding_and_oracle(tmp_path):
 
     ref_out, ref_lse = oracle.sparse_prefill(q, k, v, idx, scale=0.0625)
     compare(out_c, lse_c, ref_out, ref_lse, label="c driver")
+
+
+def test_gather_probe_rejects_bad_arguments():
+    """The gather-ceiling probe (a measuring tool built beside the library)
+    checks its arguments before any HIP call: buffer size, waves per CU and
+    loads in flight outside their ranges are refused with status 2."""
+    probe = qsa_build.PROBE
+    if not os.path.exists(probe):
+        pytest.fail("qsa_gather_probe is not built: run __graft_entry__.build() first")
+    for args in ([], ["8192", "8", "100"], ["1", "8", "100", "16"], ["4194304", "8", "100", "16"],
+                 ["8192", "6", "100", "16"], ["8192", "8", "0", "16"], ["8192", "8", "100", "12"],
+                 ["8192", "8", "100", "16", "0"]):
+        res = subprocess.run([probe, *args], capture_output=True, text=True, timeout=60)
+        assert res.returncode == 2, (args, res.stderr)

@@ -5,7 +5,9 @@
 Compiles every source under csrc/ (HIP kernels and the C ABI shim) into
 top_sparse_attention_qsa_amd/lib/libqsa.so, then the test program
 tests/c_driver/qsa_c_driver.cpp (a plain host program that calls the C ABI)
-into lib/qsa_c_driver, linked against that library, and, with g++, the host
+into lib/qsa_c_driver, linked against that library, the gather-ceiling probe
+probe/gather_probe.hip (a stand-alone measuring tool) into lib/qsa_gather_probe,
+and, with g++, the host
 check tests/c_driver/qsa_abi_sanitize.cpp (the ABI's validation under ASan
 and UBSan) into lib/qsa_abi_sanitize. Always rebuilds.
 """
@@ -24,6 +26,8 @@ DRIVER_SRC = os.path.join(ROOT, "tests", "c_driver", "qsa_c_driver.cpp")
 DRIVER = os.path.join(LIB_DIR, "qsa_c_driver")
 SANITIZE_SRC = os.path.join(ROOT, "tests", "c_driver", "qsa_abi_sanitize.cpp")
 SANITIZE = os.path.join(LIB_DIR, "qsa_abi_sanitize")
+PROBE_SRC = os.path.join(PKG, "probe", "gather_probe.hip")
+PROBE = os.path.join(LIB_DIR, "qsa_gather_probe")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
@@ -73,6 +77,11 @@ def build(verbose: bool = False) -> str:
         _run([hipcc(), *HIP_FLAGS, "-I", INCLUDE, DRIVER_SRC, "-L", LIB_DIR, "-lqsa", "-Wl,-rpath,$ORIGIN",
               "-o", tmp], verbose)
         os.replace(tmp, DRIVER)
+    if os.path.exists(PROBE_SRC):
+        # the gather-ceiling probe: a measuring tool beside the benchmark
+        tmp = PROBE + ".tmp"
+        _run([hipcc(), *HIP_FLAGS, PROBE_SRC, "-o", tmp], verbose)
+        os.replace(tmp, PROBE)
     gxx = shutil.which("g++")
     if os.path.exists(SANITIZE_SRC) and gxx:
         # host code only: the C-ABI validation under ASan/UBSan with a stub launch
