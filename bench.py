@@ -231,7 +231,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the operator "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the operator "
               "would shard over query rows or KV heads with no exchange after the kernel). "
               "Run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
