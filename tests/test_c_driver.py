@@ -94,6 +94,6 @@ def test_gather_probe_rejects_bad_arguments():
         pytest.fail("qsa_gather_probe is not built: run __graft_entry__.build() first")
     for args in ([], ["8192", "8", "100"], ["1", "8", "100", "16"], ["4194304", "8", "100", "16"],
                  ["8192", "6", "100", "16"], ["8192", "8", "0", "16"], ["8192", "8", "100", "12"],
-                 ["8192", "8", "100", "16", "0"]):
+                 ["8192", "8", "100", "16", "0"], ["8192", "8", "100", "16", "5", "1001"]):
         res = subprocess.run([probe, *args], capture_output=True, text=True, timeout=60)
         assert res.returncode == 2, (args, res.stderr)

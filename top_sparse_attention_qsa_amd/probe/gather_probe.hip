@@ -12,9 +12,11 @@
 // access stays inside the buffer (row < rows, chunk offset <= 496), which the
 // buffer descriptor's range check enforces as well.
 //
-//   qsa_gather_probe <rows> <waves_per_cu: 4|8|12|16> <iterations> <loads: 8|16|24|32> [repeats]
+//   qsa_gather_probe <rows> <waves_per_cu: 4|8|12|16> <iterations> <loads: 8|16|24|32> [repeats] [far_permille]
 // prints one line: the median over `repeats` timed launches of the bytes the
-// waves received per second.
+// waves received per second. With far_permille < 1000, each row pair comes
+// from the whole buffer with that probability and otherwise from its first
+// 8,192 rows (4 MB, which the L2s hold): a given mix of L2 hits and misses.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -26,7 +28,8 @@
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int NL>
-__global__ __launch_bounds__(256) void gather_probe(const uint8_t *buf, uint32_t rows, uint32_t iters, uint32_t *out) {
+__global__ __launch_bounds__(256) void gather_probe(const uint8_t *buf, uint32_t rows, uint32_t hot_rows,
+                                                    uint32_t far_permille, uint32_t iters, uint32_t *out) {
     const int lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)buf, 0, (int)(rows * 512u), 0x00020000);
@@ -34,10 +37,15 @@ __global__ __launch_bounds__(256) void gather_probe(const uint8_t *buf, uint32_t
     const uint32_t chunk = (uint32_t)(lane & 31) * 16u;
     const bool upper = (lane >> 5) != 0;
     auto next = [&]() -> u32x4_t {
+        // a pair of rows from the whole buffer with probability far_permille /
+        // 1000, otherwise from its first hot_rows rows
+        // (a row index is the high half of state x span: no division)
         s = s * 1664525u + 1013904223u;
-        const uint32_t r0 = (s >> 8) % rows;
+        const uint32_t span = __umulhi(s, 1000u) < far_permille ? rows : hot_rows;
         s = s * 1664525u + 1013904223u;
-        const uint32_t r1 = (s >> 8) % rows;
+        const uint32_t r0 = __umulhi(s, span);
+        s = s * 1664525u + 1013904223u;
+        const uint32_t r1 = __umulhi(s, span);
         return __builtin_amdgcn_raw_buffer_load_b128(r, (upper ? r1 : r0) * 512u + chunk, 0, 0);
     };
     // a rolling window of NL loads: each step folds the oldest load's data
@@ -76,13 +84,15 @@ int main(int argc, char **argv) {
     const long iters_l = atol(argv[3]);
     const int nl = atoi(argv[4]);
     const int repeats = argc > 5 ? atoi(argv[5]) : 5;
+    const long far_l = argc > 6 ? atol(argv[6]) : 1000;
     if (rows_l < 2 || rows_l * 512L >= (1L << 31) || iters_l < 1 || iters_l > 100000 || repeats < 1 ||
         repeats > 50 || (wpc != 4 && wpc != 8 && wpc != 12 && wpc != 16) ||
-        (nl != 8 && nl != 16 && nl != 24 && nl != 32)) {
+        (nl != 8 && nl != 16 && nl != 24 && nl != 32) || far_l < 0 || far_l > 1000) {
         fprintf(stderr, "argument out of range\n");
         return 2;
     }
-    const uint32_t rows = (uint32_t)rows_l, iters = (uint32_t)iters_l;
+    const uint32_t rows = (uint32_t)rows_l, iters = (uint32_t)iters_l, far = (uint32_t)far_l;
+    const uint32_t hot = rows < 8192u ? rows : 8192u;
     hipDeviceProp_t prop;
     hipError_t e = hipGetDeviceProperties(&prop, 0);
     if (e != hipSuccess) return fail("hipGetDeviceProperties", e);
@@ -99,12 +109,12 @@ int main(int argc, char **argv) {
     hipEvent_t e0, e1;
     if ((e = hipEventCreate(&e0)) != hipSuccess || (e = hipEventCreate(&e1)) != hipSuccess)
         return fail("hipEventCreate", e);
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), lds, 0, (const uint8_t *)buf, rows, 2u, out);
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), lds, 0, (const uint8_t *)buf, rows, hot, far, 2u, out);
     if ((e = hipDeviceSynchronize()) != hipSuccess) return fail("warm-up", e);
     std::vector<float> ms(repeats);
     for (int rep = 0; rep < repeats; ++rep) {
         (void)hipEventRecord(e0, 0);
-        hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), lds, 0, (const uint8_t *)buf, rows, iters, out);
+        hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), lds, 0, (const uint8_t *)buf, rows, hot, far, iters, out);
         (void)hipEventRecord(e1, 0);
         if ((e = hipEventSynchronize(e1)) != hipSuccess) return fail("launch", e);
         (void)hipEventElapsedTime(&ms[rep], e0, e1);
@@ -112,9 +122,9 @@ int main(int argc, char **argv) {
     std::sort(ms.begin(), ms.end());
     const float med = ms[repeats / 2];
     const double bytes = (double)blocks * 4 * ((double)iters + 1) * nl * 1024;
-    printf("gather probe: rows %u (%.1f MB), %d waves/CU, %d loads in flight per wave (%d KB per CU): "
-           "median %.3f ms of %d, %.2f TB/s\n",
-           rows, rows * 512.0 / 1e6, wpc, nl, wpc * nl, med, repeats, bytes / (med * 1e-3) / 1e12);
+    printf("gather probe: rows %u (%.1f MB), %d waves/CU, %d loads in flight per wave (%d KB per CU), "
+           "%.1f%% of row pairs from the whole buffer: median %.3f ms of %d, %.2f TB/s\n",
+           rows, rows * 512.0 / 1e6, wpc, nl, wpc * nl, far / 10.0, med, repeats, bytes / (med * 1e-3) / 1e12);
     (void)hipFree(buf);
     (void)hipFree(out);
     return 0;
