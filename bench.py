@@ -178,7 +178,8 @@ def load_inputs(cfg):
 
 
 def cpu_baseline(cfg, d, n_rows: int):
-    """The fp64 oracle, as it is, on a seeded sample of the workload's rows."""
+    """The fp64 oracle, as it is, on a seeded sample of the workload's rows:
+    ((rows, out, lse) it computed, the timing record)."""
     from oracle import pool
     from qsa_inputs import PoolConfig, sample_pool_rows, sample_rows
 
@@ -191,9 +192,10 @@ def cpu_baseline(cfg, d, n_rows: int):
     rows = rows[:n_rows]
     workers = pool.default_workers()
     affinity = pool.affinity_cpus()
-    _, _, secs = pool.run_rows(d["q"], d["k"], d["v"], d["idx"][rows], rows, cfg.scale, workers=workers,
-                               return_seconds=True, **kw)
-    return {
+    ref_out, ref_lse, secs = pool.run_rows(d["q"], d["k"], d["v"], d["idx"][rows], rows, cfg.scale,
+                                           workers=workers, return_seconds=True, **kw)
+    reference = (rows, ref_out, ref_lse)
+    return reference, {
         "value": round(float(rows.size / secs), 3),
         "unit": "query-tokens/s",
         "cores": workers,
@@ -202,6 +204,35 @@ def cpu_baseline(cfg, d, n_rows: int):
         "sample": f"{rows.size} seeded rows of {cfg.name} (all {cfg.Hq} heads each), fp64 NumPy, "
                   f"{workers} processes (one per core; {affinity} CPUs in this process's affinity set, "
                   f"at most {pool.MAX_WORKERS} used), BLAS single-threaded; {secs:.2f} s wall",
+    }
+
+
+def parity_record(rows, ref_out, ref_lse, out_bits, lse):
+    """The GPU's outputs on the rows the CPU baseline computed, against the
+    oracle's: max |out| and |lse| errors, rel-L2, and whether every element
+    is within 1e-2 plus half a bf16 ulp of the oracle (every finite lse within
+    1e-3, every empty row +0.0 with lse -inf on both sides)."""
+    import numpy as np
+
+    g = (np.asarray(out_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    g = g.astype(np.float64)
+    err = np.abs(g - ref_out)
+    _, ex = np.frexp(np.abs(ref_out))
+    bound = 1e-2 + np.ldexp(1.0, np.maximum(ex, -125) - 9)
+    fin = np.isfinite(ref_lse)
+    lse = np.asarray(lse, dtype=np.float64)
+    lerr = np.abs(lse[fin] - ref_lse[fin])
+    same_empty = bool(np.array_equal(np.isfinite(lse), fin) and np.all(lse[~fin] == ref_lse[~fin]))
+    outside = int(np.count_nonzero(err > bound))
+    max_lse = float(lerr.max()) if lerr.size else 0.0
+    return {
+        "rows_checked": int(np.asarray(rows).size),
+        "max_abs_out": float(err.max()) if err.size else 0.0,
+        "max_abs_lse": max_lse,
+        "rel_l2": float(np.linalg.norm(g - ref_out) / max(np.linalg.norm(ref_out), 1e-300)) if err.size else 0.0,
+        "outside_bar": outside,
+        "within_bar": bool(outside == 0 and max_lse <= 1e-3 and same_empty),
+        "bar": "|out - oracle| <= 1e-2 + half a bf16 ulp of the oracle; |lse - oracle| <= 1e-3 on finite lse",
     }
 
 
@@ -249,10 +280,10 @@ def main():
     d = load_inputs(cfg)
     log(f"{cfg.name}: inputs generated in {time.perf_counter() - t0:.1f}s")
 
-    cpu = None
+    cpu = reference = None
     if not args.no_cpu_baseline and args.cpu_rows > 0:
         t0 = time.perf_counter()
-        cpu = cpu_baseline(cfg, d, args.cpu_rows)
+        reference, cpu = cpu_baseline(cfg, d, args.cpu_rows)
         log(f"cpu baseline {cpu['value']} q-tok/s on {cpu['cores']} cores ({time.perf_counter() - t0:.1f}s)")
 
     if not torch.cuda.is_available():
@@ -351,6 +382,16 @@ def main():
     qtok_s = cfg.T / (ms_per_step * 1e-3)
     logical_gbps = gathered / (ms_per_step * 1e-3) / 1e9
 
+    # the outputs of the last timed call, on the rows the oracle computed
+    parity = None
+    if reference is not None:
+        rows_chk, ref_out, ref_lse = reference
+        sel = torch.from_numpy(np.asarray(rows_chk, dtype=np.int64)).to(dev)
+        got = out.index_select(0, sel).view(torch.int16).cpu().numpy().view(np.uint16)
+        got_lse = lse.index_select(0, sel).cpu().numpy()
+        parity = parity_record(rows_chk, ref_out, ref_lse, got, got_lse)
+        del ref_out, ref_lse, reference
+
     roofline, past_l2 = roofline_records(gathered, kernel_s, counters)
     if ceiling:
         roofline["measured_ceiling"] = {
@@ -388,6 +429,10 @@ def main():
                           "note": "PyTorch allocator peak over the timed calls: resident inputs, outputs "
                                   "and any decode workspace; the library itself allocates nothing"},
         "cpu_baseline": cpu,
+        "parity": parity,
+        "device": {"name": torch.cuda.get_device_name(dev),
+                   "arch": getattr(torch.cuda.get_device_properties(dev), "gcnArchName", None),
+                   "hip": torch.version.hip, "torch": torch.__version__},
         "gpu_over_cpu": round(qtok_s / cpu["value"], 1) if cpu else None,
     }
     print(json.dumps(res), flush=True)

@@ -101,3 +101,26 @@ def test_probe_output_is_parsed():
             "median 1.086 ms of 5, 24.72 TB/s\n")
     assert bench.parse_probe(line) == pytest.approx(24720.0)
     assert bench.parse_probe("nothing") is None
+
+
+def test_parity_record_applies_the_bar():
+    """bench.py compares the GPU's outputs on the CPU baseline's rows with the
+    oracle's: bf16 rounding of the exact value passes, an error of 0.02
+    fails, and an empty row must be +0.0 with lse = -inf on both sides."""
+    import numpy as np
+    from qsa_inputs import f32_to_bf16_bits
+    rng = np.random.default_rng(0)
+    ref = rng.standard_normal((5, 3, 256)) * 3
+    ref_lse = rng.standard_normal((5, 3))
+    ref_lse[4] = -np.inf
+    ref[4] = 0.0
+    bits = f32_to_bf16_bits(ref.astype(np.float32))
+    lse = ref_lse.astype(np.float32)
+    rec = bench.parity_record(np.arange(5), ref, ref_lse, bits, lse)
+    assert rec["within_bar"] and rec["outside_bar"] == 0 and rec["rows_checked"] == 5
+    assert 0 < rec["max_abs_out"] <= 2 ** -4 and rec["max_abs_lse"] < 1e-6  # half an ulp reaches 2^-5 at |o| >= 8
+    bad = f32_to_bf16_bits((ref + 0.02 * (np.abs(ref) < 1)).astype(np.float32))
+    assert not bench.parity_record(np.arange(5), ref, ref_lse, bad, lse)["within_bar"]
+    lse_bad = lse.copy()
+    lse_bad[4, 0] = 0.0
+    assert not bench.parity_record(np.arange(5), ref, ref_lse, bits, lse_bad)["within_bar"]
