@@ -222,7 +222,9 @@ qsa_status_t qsa_sparse_decode(const void *q, const void *k_pool, const void *v_
  *
  * The scratch is QSA_DECODE_SCRATCH_BYTES (16 MiB) per GPU, held from the
  * library's load until the process ends; the first call on a device looks up
- * that device's copy. Every valid size fits it: the split plan never needs
+ * that device's copy (a runtime query that may load the library's code on that
+ * device), so make one call on each device before capturing calls in a HIP
+ * graph. Every valid size fits it: the split plan never needs
  * more than about 12.8 MB (at most 16 * 767 partial rows of 1,040 bytes).
  * Every call on one GPU shares that GPU's scratch, so calls that overlap on
  * one GPU (e.g. on two streams at once) race and give undefined results;
