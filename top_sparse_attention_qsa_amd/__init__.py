@@ -305,8 +305,10 @@ def sparse_decode_noalloc(q, k_pool, v_pool, slot_idx, q_pos, slot_pos, scale=No
     scratch (16 MiB per GPU, held until the process ends) instead of a
     workspace: the library call allocates no memory. Results are bit-identical
     to sparse_decode. Calls that overlap on one GPU (two streams at once) race
-    on the scratch; calls on one stream are safe. Pass `out` and `lse` to keep
-    the whole call free of allocation (this binding allocates them otherwise)."""
+    on the scratch; calls on one stream are safe. Pass contiguous inputs and
+    `out` and `lse` to keep the whole call free of allocation (this binding
+    allocates the outputs, and contiguous copies of strided inputs,
+    otherwise)."""
     lib = load_library()
     q, k_pool, v_pool, slot_idx, scale, out, lse, stream = _prepare(q, k_pool, v_pool, slot_idx, scale,
                                                                     out, lse)
