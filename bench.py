@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the QSA sparse-prefill operator on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload c4]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload c4] [--graph]
 
 A step is one call of the operator over the whole workload (all query tokens,
 all heads): gather the selected K/V rows, scores, softmax, weighted values,
@@ -37,6 +37,11 @@ micro-block workloads c7/c8 (entries name 4-token blocks, the model's
 compression ratio), the ragged slot-pool batches c9/c10/c13 and the decode
 batches c11/c12 (one query per request; the step includes the merge of the
 split lists). Each is timed the same way through its own entry point.
+
+With --graph the timed calls are replayed from a captured HIP graph rather
+than launched one host call at a time; the microsecond workloads are
+otherwise bound by the host's per-call work. The line's `launch` field says
+which.
 """
 import argparse
 import hashlib
@@ -259,6 +264,11 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=32768,
                     help="rows for the oracle CPU baseline (all 32,768 rows of the default workload: about 9 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="launch the timed calls from a captured HIP graph (the timed region replays one graph of "
+                         "--steps calls) instead of one host call each: the same kernels without the host's "
+                         "per-call work, as a serving loop would run them (the per-launch pass stays eager: "
+                         "a one-call graph adds the graph's own launch time)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -349,6 +359,20 @@ def main():
     torch.cuda.synchronize()
     first_ms = cold0.elapsed_time(cold1)
 
+    if args.graph:
+        # the same calls, captured after the warm-up (the library allocates
+        # nothing and never synchronises, so every call is capturable)
+        graph_all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph_all):
+            for _ in range(args.steps):
+                step()
+        torch.cuda.synchronize()
+        timed_calls = graph_all.replay
+    else:
+        def timed_calls():
+            for _ in range(args.steps):
+                step()
+
     # the timed region: K steps back to back, one HIP event pair around them
     # (an event pair per step costs host time that a microsecond decode step
     # would show)
@@ -356,8 +380,7 @@ def main():
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     r0.record(stream)
-    for _ in range(args.steps):
-        step()
+    timed_calls()
     r1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -416,6 +439,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": workload_config(cfg),
+        "launch": "hip_graph" if args.graph else "eager",
         "gathered_kv_GBps": round(logical_gbps, 1),
         "hbm_roofline_frac": round(logical_gbps / HBM_PEAK_GBPS, 4),
         "copy_roofline_frac": round(logical_gbps / copy_gbps, 4),
