@@ -395,6 +395,9 @@ def main():
         e1.record(stream)
     torch.cuda.synchronize()
     kms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    # the allocator's peak over the calls (read before the parity check below,
+    # whose row gathers allocate copies of the outputs)
+    peak_bytes = int(torch.cuda.max_memory_allocated(dev))
 
     ms_per_step = wall * 1e3 / args.steps
     gathered = cfg.gathered_bytes()
@@ -448,8 +451,8 @@ def main():
         "first_call_ms": round(first_ms, 3),
         "copy_GBps": round(copy_gbps, 1),
         "useful_tflops": round(cfg.useful_flops() / kernel_s / 1e12, 2),
-        "device_memory": {"max_allocated_bytes": int(torch.cuda.max_memory_allocated(dev)),
-                          "max_allocated_MiB": round(torch.cuda.max_memory_allocated(dev) / 2 ** 20, 1),
+        "device_memory": {"max_allocated_bytes": peak_bytes,
+                          "max_allocated_MiB": round(peak_bytes / 2 ** 20, 1),
                           "note": "PyTorch allocator peak over the timed calls: resident inputs, outputs "
                                   "and any decode workspace; the library itself allocates nothing"},
         "cpu_baseline": cpu,
