@@ -7,8 +7,10 @@ outputs must equal qsa_sparse_decode's bit for bit, and meet the oracle bar
 smaller batch than the one before, so each runs over the scratch contents
 the previous call left behind; a batch with enough lists that they are not
 cut uses no scratch at all. A call captured in a HIP graph replays bit for
-bit with other calls in between.
+bit with other calls in between, through PyTorch's graph capture and from a
+plain host program that captures it with the HIP runtime alone.
 """
+import os
 import sys
 import time
 
@@ -138,3 +140,37 @@ def test_noalloc_decode_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ro.view(torch.int16)), i
         assert torch.equal(lse.view(torch.int32), rl.view(torch.int32)), i
+
+
+def test_noalloc_decode_from_a_plain_hip_graph(tmp_path):
+    """A plain host program (tests/c_driver/qsa_c_driver.cpp --decode): its
+    own hipMalloc buffers and stream, no PyTorch in the process. It makes
+    one call, then captures the same call with hipStreamBeginCapture and
+    launches the graph twice; the program itself requires every launch to
+    reproduce the first call's bits. Its output must also equal the binding's
+    qsa_sparse_decode (caller workspace) bit for bit and meet the oracle bar."""
+    import subprocess
+
+    from top_sparse_attention_qsa_amd import build as qsa_build
+
+    if not os.path.exists(qsa_build.DRIVER):
+        pytest.fail("qsa_c_driver is not built: run __graft_entry__.build() first")
+    d = small_batch(9, n_req=3, Hq=12, Hkv=2, K=1500, n_slots=5000)
+    n_req, Hq, Hkv, K = 3, 12, 2, 1500
+    assert qsa.decode_workspace_bytes(n_req, Hq, Hkv, K) > 0  # the lists are cut: the scratch is used
+    (tmp_path / "meta.txt").write_text(f"{n_req} {Hq} {Hkv} {K} {d['k'].shape[0]} {d['scale']}\n")
+    for name, key in (("q", "q"), ("k", "k"), ("v", "v"), ("idx", "idx"), ("qpos", "q_pos"), ("spos", "slot_pos")):
+        np.ascontiguousarray(d[key]).tofile(tmp_path / f"{name}.bin")
+    progress("plain-HIP graph decode: running qsa_c_driver --decode")
+    res = subprocess.run([qsa_build.DRIVER, "--decode", str(tmp_path)], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr
+    out_c = np.fromfile(tmp_path / "out.bin", dtype=np.uint16).reshape(n_req, Hq, 256)
+    lse_c = np.fromfile(tmp_path / "lse.bin", dtype=np.float32).reshape(n_req, Hq)
+    ro, rl = qsa.sparse_decode(*device_batch(d), scale=d["scale"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out_c, torch_bf16_to_numpy_bits(ro))
+    np.testing.assert_array_equal(lse_c.view(np.int32), rl.cpu().numpy().view(np.int32))
+    ref_out, ref_lse = oracle.sparse_prefill_pool(d["q"], d["k"], d["v"], d["idx"], d["q_pos"], d["slot_pos"],
+                                                  scale=d["scale"])
+    stats = compare(out_c, lse_c, ref_out, ref_lse, label="plain-HIP graph decode")
+    progress(f"plain-HIP graph decode: {res.stdout.strip()}; {stats}")
