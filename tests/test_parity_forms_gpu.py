@@ -621,6 +621,38 @@ def test_pool_extreme_positions():
     assert np.all(np.isneginf(lse[2]))
 
 
+QSA_MAX_LIST = 1 << 28  # include/qsa.h: the widest index list accepted
+
+
+def test_widest_index_list():
+    """K = 2^28 entries per list, the widest the ABI accepts: each (row, KV
+    head) list is 1 GiB of int32, its entries addressed with byte offsets up to
+    2^30. The few usable entries sit at the very end of the lists, at 2^27 and
+    near the start, among pads, other negatives and a future position; a wave
+    walks all 2^24 tiles of its list. The oracle gets the same entries in the
+    same order without the pads (pads change nothing: pinned)."""
+    T, Hq, Hkv, K = 2, 4, 1, QSA_MAX_LIST
+    rng = np.random.default_rng(930)
+    q, k, v = rand_bf16(rng, (T, Hq, 256)), rand_bf16(rng, (T, Hkv, 256)), rand_bf16(rng, (T, Hkv, 256))
+    # (list position, entry) per row; every other position holds -1
+    entries = [[(12345, 0), (K - 2, 1), (K - 1, 0)],             # 1 is after row 0: masked
+               [(5, -7), (1 << 27, 1), (K - 17, 0), (K - 1, 1)]]
+    idx = torch.full((T, Hkv, K), -1, dtype=torch.int32, device="cuda")
+    short = np.full((T, Hkv, 4), -1, np.int32)
+    for t, row in enumerate(entries):
+        for i, (at, val) in enumerate(row):
+            idx[t, 0, at] = val
+            short[t, 0, i] = val
+    progress(f"widest list: K = 2^28 ({T * K * 4 / 2**30:.0f} GiB of indices), one wave per row walks 2^24 tiles")
+    t0 = time.time()
+    out, lse = host(*qsa.sparse_prefill(dev_bf16(q), dev_bf16(k), dev_bf16(v), idx))
+    secs = time.time() - t0
+    del idx
+    torch.cuda.empty_cache()
+    ref_out, ref_lse = oracle.sparse_prefill(q, k, v, short)
+    progress(f"widest list: {secs:.1f} s; {compare(out, lse, ref_out, ref_lse, label='K = 2^28')}")
+
+
 # ------------------------------------------------------------------ graph capture
 
 
